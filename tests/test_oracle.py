@@ -1,0 +1,405 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Library routines (torch casts, torch SDPA, index_copy_), closed forms,
+hand-worked fixtures under tests/golden/ and invariants.  Each test is chosen
+so that a plausible slip in the oracle (a dropped scale, a wrong sign, a wrong
+GQA index, a transposed operand, an off-by-one length) fails it.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# --------------------------------------------------------------------------- storage
+
+
+def test_e4m3fn_table_matches_torch_cast():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = orc.e4m3fn_table()
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def test_bf16_decode_matches_torch_view():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    mine = orc.decode_bf16(bits)
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+
+
+def test_fp8_scaled_decode_matches_torch():
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 256, size=(6, 4), dtype=np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0
+    scale = rng.uniform(0.01, 2.0, size=(6, 1)).astype(np.float32)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale.astype(np.float64)
+    assert np.array_equal(orc.decode_e4m3fn(codes, scale), ref)
+
+
+# --------------------------------------------------------------------------- scatter
+
+
+@pytest.mark.parametrize("np_dtype", [np.float32, np.uint16, np.uint8])
+@pytest.mark.parametrize("with_idx", [False, True])
+@pytest.mark.parametrize("with_second", [False, True])
+def test_scatter_matches_index_copy(np_dtype, with_idx, with_second):
+    rng = np.random.default_rng(2)
+    pages, ps, hkv, d = 7, 8, 3, 16
+    if np_dtype == np.float32:
+        pool = rng.standard_normal((pages, ps, hkv, d)).astype(np.float32)
+        src = rng.standard_normal((20, hkv, d)).astype(np.float32)
+    else:
+        info = np.iinfo(np_dtype)
+        pool = rng.integers(0, info.max, size=(pages, ps, hkv, d)).astype(np_dtype)
+        src = rng.integers(0, info.max, size=(20, hkv, d)).astype(np_dtype)
+    n = 12
+    perm = rng.permutation(pages * ps)
+    slots = perm[:n].astype(np.int64)
+    slots[[3, 7]] = -1                      # skipped tokens
+    slots2 = perm[n:2 * n].astype(np.int64) if with_second else None
+    if with_second:
+        slots2[5] = -4
+    src_idx = rng.permutation(20)[:n] if with_idx else None
+    mine = orc.scatter_slots(pool, src, slots, src_idx=src_idx, slots2=slots2)
+
+    as_t = lambda a: torch.from_numpy(a.view(np.int32) if a.dtype == np.float32 else a.astype(np.int32))
+    flat = as_t(pool.copy()).reshape(pages * ps, hkv, d)
+    srows = as_t(src)[torch.from_numpy(src_idx) if with_idx else torch.arange(20)[:n]]
+    for dst in ([slots] if slots2 is None else [slots, slots2]):
+        keep = torch.from_numpy(dst >= 0)
+        flat.index_copy_(0, torch.from_numpy(dst)[keep], srows[keep])
+    assert np.array_equal(as_t(mine).reshape(pages * ps, hkv, d).numpy(), flat.numpy())
+
+
+# --------------------------------------------------------------------------- table translation
+
+
+def test_gather_matches_hand_worked_slot_fixture():
+    rows = _read_golden("slot_mapping.txt")
+    ps = int(rows[0][1])
+    table = np.array([int(x) for x in rows[1][1:]])
+    length = int(rows[2][1])
+    expect = np.array([[int(x) for x in r] for r in rows[3:]])
+    pages = 8
+    # every pool row carries its own slot id as its value
+    pool = np.arange(pages * ps, dtype=np.int64).reshape(pages, ps, 1, 1)
+    got = orc.gather_logical(pool, table, length)[:, 0, 0]
+    assert got.tolist() == expect[:, 3].tolist()
+    assert (got // ps).tolist() == expect[:, 1].tolist()
+    assert (got % ps).tolist() == expect[:, 2].tolist()
+
+
+def test_gather_is_page_permutation_invariant():
+    rng = np.random.default_rng(3)
+    ps, hkv, d, length = 4, 2, 3, 13
+    logical = rng.standard_normal((length, hkv, d))
+    n_pages = math.ceil(length / ps)
+    for seed in range(3):
+        order = np.random.default_rng(seed).permutation(10)[:n_pages]
+        pool = np.full((10, ps, hkv, d), np.nan)
+        for j, page in enumerate(order):           # page-wise placement, block copies
+            chunk = logical[j * ps:(j + 1) * ps]
+            pool[page, :len(chunk)] = chunk
+        table = np.concatenate([order, [-12345]])  # trailing entry must never be read
+        assert np.array_equal(orc.gather_logical(pool, table, length), logical)
+
+
+# --------------------------------------------------------------------------- attention
+
+
+def _sdpa(q, k, v, scale, mask=None, gqa=False):
+    """torch SDPA in float64 on the CPU; q [..., R, D], k/v [..., L, D]."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=None if mask is None else torch.from_numpy(mask), scale=scale, enable_gqa=gqa)
+    return out.numpy()
+
+
+def test_attention_matches_torch_sdpa_and_logsumexp():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((5, 16))
+    k = rng.standard_normal((37, 16))
+    v = rng.standard_normal((37, 16))
+    scale = 0.37
+    o, lse = orc.attention_rows(q, k, v, scale)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, scale), rtol=0, atol=1e-12)
+    ref_lse = torch.logsumexp(torch.from_numpy(scale * q @ k.T), dim=1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 8))
+    k = rng.standard_normal((2, 8))
+    v = rng.standard_normal((2, 8))
+    scale = 0.5
+    # one key: the output is that value, the LSE its score
+    o, lse = orc.attention_rows(q, k[:1], v[:1], scale)
+    np.testing.assert_allclose(o[0], v[0], atol=1e-15)
+    np.testing.assert_allclose(lse[0], scale * float(q[0] @ k[0]), atol=1e-15)
+    # two keys: logistic weight of the score difference
+    s0, s1 = scale * float(q[0] @ k[0]), scale * float(q[0] @ k[1])
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    o, lse = orc.attention_rows(q, k, v, scale)
+    np.testing.assert_allclose(o[0], w0 * v[0] + (1 - w0) * v[1], atol=1e-14)
+    np.testing.assert_allclose(lse[0], math.log(math.exp(s0) + math.exp(s1)), atol=1e-14)
+    # zero query: uniform weights, the output is the mean value and LSE = ln L
+    o, lse = orc.attention_rows(np.zeros((1, 8)), k, v, scale)
+    np.testing.assert_allclose(o[0], v.mean(axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse[0], math.log(2), atol=1e-15)
+    # no keys: zero output, LSE -inf
+    o, lse = orc.attention_rows(q, k[:0], v[:0], scale)
+    assert np.all(o == 0) and np.isneginf(lse[0])
+
+
+def test_attention_peaked_key_dominates():
+    rng = np.random.default_rng(6)
+    d, length = 16, 40
+    k = rng.standard_normal((length, d)) * 0.1
+    v = rng.standard_normal((length, d))
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    k[23, 0] = 60.0   # score 60 * scale above the rest
+    o, _ = orc.attention_rows(q, k, v, 1.0)
+    np.testing.assert_allclose(o[0], v[23], atol=1e-20 + 1e-12)
+
+
+def _paged_pool_from_logical(rng, logical_k, logical_v, ps, n_pool, poison=np.nan):
+    """Place logical keys of each sequence on random pages, page by page."""
+    n_t = len(logical_k)
+    hkv, d = logical_k[0].shape[1:]
+    perm = rng.permutation(n_pool)
+    kp = np.full((n_pool, ps, hkv, d), poison)
+    vp = np.full((n_pool, ps, hkv, d), poison)
+    width = max(math.ceil(len(x) / ps) for x in logical_k) + 1
+    tables = np.full((n_t, width), perm[-1], dtype=np.int64)
+    at = 0
+    for t in range(n_t):
+        for j in range(math.ceil(len(logical_k[t]) / ps)):
+            page = perm[at]
+            at += 1
+            tables[t, j] = page
+            kc = logical_k[t][j * ps:(j + 1) * ps]
+            kp[page, :len(kc)] = kc
+            vp[page, :len(kc)] = logical_v[t][j * ps:(j + 1) * ps]
+    return kp.astype(np.float32), vp.astype(np.float32), tables
+
+
+@pytest.mark.parametrize("hq,hkv,n_rows", [(4, 4, 1), (4, 2, 1), (8, 2, 3)])
+def test_decode_matches_sdpa_over_contiguous_keys(hq, hkv, n_rows):
+    rng = np.random.default_rng(7)
+    d, ps = 8, 4
+    lens = [9, 1, 16, 0]
+    lk = [rng.standard_normal((L, hkv, d)).astype(np.float32).astype(np.float64) for L in lens]
+    lv = [rng.standard_normal((L, hkv, d)).astype(np.float32).astype(np.float64) for L in lens]
+    kp, vp, tables = _paged_pool_from_logical(rng, lk, lv, ps, 16)
+    q = rng.standard_normal((len(lens), n_rows, hq, d)).astype(np.float32)
+    scale = 0.41
+    out, lse = orc.attn_decode(kp, vp, q, tables, np.array(lens), scale, kv_dtype="f32")
+    assert np.all(np.isfinite(out))              # poison is never read
+    for t, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[t] == 0) and np.all(np.isneginf(lse[t]))
+            continue
+        qt = q[t].astype(np.float64).transpose(1, 0, 2)          # [Hq, n, D]
+        kt = lk[t].transpose(1, 0, 2)                            # [Hkv, L, D]
+        vt = lv[t].transpose(1, 0, 2)
+        ref = _sdpa(qt, kt, vt, scale, gqa=(hq != hkv))          # [Hq, n, D]
+        np.testing.assert_allclose(out[t].transpose(1, 0, 2), ref, atol=1e-12)
+
+
+def test_decode_fp8_matches_torch_dequant():
+    rng = np.random.default_rng(8)
+    ps, hkv, d, hq = 4, 2, 8, 4
+    n_pool = 6
+    codes_k = rng.integers(0, 0x7E, size=(n_pool, ps, hkv, d), dtype=np.uint8)
+    codes_v = rng.integers(0, 0x7E, size=(n_pool, ps, hkv, d), dtype=np.uint8)
+    codes_k |= (rng.integers(0, 2, size=codes_k.shape, dtype=np.uint8) << 7)
+    sk = rng.uniform(0.001, 0.02, size=(n_pool, hkv)).astype(np.float32)
+    sv = rng.uniform(0.001, 0.02, size=(n_pool, hkv)).astype(np.float32)
+    table = np.array([[4, 1, 3]])
+    L = 10
+    q = to_bf16_bits(rng.standard_normal((1, 1, hq, d)).astype(np.float32))
+    out, lse = orc.attn_decode(codes_k, codes_v, q, table, [L], 0.3, kv_dtype="fp8", k_scale=sk, v_scale=sv)
+    deq = lambda c, s: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy() * \
+        s.astype(np.float64)[:, None, :, None]
+    kr = deq(codes_k, sk)[[4, 1, 3]].reshape(3 * ps, hkv, d)[:L]
+    vr = deq(codes_v, sv)[[4, 1, 3]].reshape(3 * ps, hkv, d)[:L]
+    qf = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ref = _sdpa(qf[0].transpose(1, 0, 2), kr.transpose(1, 0, 2), vr.transpose(1, 0, 2), 0.3, gqa=True)
+    np.testing.assert_allclose(out[0].transpose(1, 0, 2), ref, atol=1e-12)
+
+
+def to_bf16_bits(x):
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+def _visibility_cases():
+    rows = _read_golden("prefill_visibility.txt")
+    cases = []
+    for i in range(0, len(rows), 2):
+        _, n_ctx, seq_len, cbs, s_q = rows[i]
+        cases.append((int(n_ctx), int(seq_len), int(cbs), int(s_q), [int(x) for x in rows[i + 1]]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _visibility_cases())
+def test_prefill_visibility_matches_hand_worked_fixture(case):
+    n_ctx, seq_len, cbs, s_q, counts = case
+    assert [orc.prefill_visible_keys(i, n_ctx, seq_len, cbs) for i in range(s_q)] == counts
+
+
+@pytest.mark.parametrize("case", _visibility_cases())
+def test_prefill_zero_query_one_hot_values_reveal_visible_set(case):
+    """q = 0 makes every visible score equal, so with one-hot V rows the output
+    is 1/count on each visible key's coordinate and 0 elsewhere."""
+    n_ctx, seq_len, cbs, s_q, counts = case
+    ps = 2
+    total = n_ctx + seq_len
+    d = max(total, 1)
+    n_pages = math.ceil(total / ps)
+    order = np.random.default_rng(9).permutation(n_pages + 3)[:n_pages]
+    kp = np.full((n_pages + 3, ps, 1, d), np.nan, dtype=np.float32)
+    vp = np.full((n_pages + 3, ps, 1, d), np.nan, dtype=np.float32)
+    eye = np.eye(d, dtype=np.float32)
+    for j, page in enumerate(order):
+        for r in range(ps):
+            p = j * ps + r
+            if p < total:
+                kp[page, r, 0] = 1.0
+                vp[page, r, 0] = eye[p]
+    table = np.concatenate([order, [order[0]]])[None]
+    q = np.zeros((1, s_q, 1, d), dtype=np.float32)
+    out, lse = orc.attn_prefill_block_causal(kp, vp, q, table, [n_ctx], [seq_len], cbs, 1.0, kv_dtype="f32")
+    for i, c in enumerate(counts):
+        expect = np.zeros(d)
+        expect[:c] = 1.0 / c if c else 0.0
+        np.testing.assert_allclose(out[0, i, 0], expect, atol=1e-15)
+        if c == 0:
+            assert np.isneginf(lse[0, i, 0])
+        else:
+            np.testing.assert_allclose(lse[0, i, 0], math.log(c), atol=1e-15)
+
+
+def test_prefill_one_token_blocks_is_causal_sdpa():
+    rng = np.random.default_rng(10)
+    s, h, d, ps = 11, 2, 8, 4
+    k = rng.standard_normal((s, h, d)).astype(np.float32)
+    v = rng.standard_normal((s, h, d)).astype(np.float32)
+    kp, vp, tables = _paged_pool_from_logical(rng, [k.astype(np.float64)], [v.astype(np.float64)], ps, 8)
+    q = rng.standard_normal((1, s, h, d)).astype(np.float32)
+    out, _ = orc.attn_prefill_block_causal(kp, vp, q, tables, [0], [s], 1, 0.3, kv_dtype="f32")
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[0].transpose(1, 0, 2)).double(), torch.from_numpy(k.transpose(1, 0, 2)).double(),
+        torch.from_numpy(v.transpose(1, 0, 2)).double(), is_causal=True, scale=0.3).numpy()
+    np.testing.assert_allclose(out[0].transpose(1, 0, 2), ref, atol=1e-12)
+
+
+def test_prefill_matches_masked_sdpa_with_context_and_gqa():
+    rng = np.random.default_rng(11)
+    n_ctx, seq_len, s_q, cbs, hq, hkv, d, ps = 6, 7, 9, 3, 4, 2, 8, 4
+    total = n_ctx + seq_len
+    k = rng.standard_normal((total, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((total, hkv, d)).astype(np.float32)
+    kp, vp, tables = _paged_pool_from_logical(rng, [k.astype(np.float64)], [v.astype(np.float64)], ps, 8)
+    q = rng.standard_normal((1, s_q, hq, d)).astype(np.float32)
+    out, lse = orc.attn_prefill_block_causal(kp, vp, q, tables, [n_ctx], [seq_len], cbs, 0.25, kv_dtype="f32")
+    counts = [9, 9, 9, 12, 12, 12, 13, 0, 0]  # by hand: n_ctx 6 + {3, 6, 7}; rows 7, 8 are padding
+    mask = np.zeros((s_q, total), dtype=bool)
+    for i, c in enumerate(counts):
+        mask[i, :c] = True
+    real = np.array([c > 0 for c in counts])
+    ref = _sdpa(q[0].transpose(1, 0, 2)[:, real].astype(np.float64), k.transpose(1, 0, 2).astype(np.float64),
+                v.transpose(1, 0, 2).astype(np.float64), 0.25, mask=mask[real], gqa=True)
+    np.testing.assert_allclose(out[0, real].transpose(1, 0, 2), ref, atol=1e-12)
+    assert np.all(out[0, ~real] == 0) and np.all(np.isneginf(lse[0, ~real]))
+
+
+# --------------------------------------------------------------------------- merge
+
+
+def test_merge_hand_worked_fixture():
+    rows = {r[0]: [float(x) for x in r[1:]] for r in _read_golden("merge_two_states.txt")}
+    o, lse = orc.merge_states(np.array([[rows["o1"]], [rows["o2"]]]), np.array([rows["lse1"], rows["lse2"]]))
+    np.testing.assert_allclose(o[0], rows["o"], atol=1e-15)
+    np.testing.assert_allclose(lse[0], rows["lse"][0], atol=1e-15)
+
+
+@pytest.mark.parametrize("n_chunks", [1, 2, 5])
+def test_merge_of_chunks_equals_whole(n_chunks):
+    rng = np.random.default_rng(12 + n_chunks)
+    q = rng.standard_normal((3, 8))
+    k = rng.standard_normal((50, 8))
+    v = rng.standard_normal((50, 8))
+    cuts = np.sort(rng.choice(np.arange(1, 50), size=n_chunks - 1, replace=False))
+    bounds = [0, *cuts.tolist(), 50]
+    parts = [orc.attention_rows(q, k[a:b], v[a:b], 0.7) for a, b in zip(bounds[:-1], bounds[1:])]
+    parts.append(orc.attention_rows(q, k[:0], v[:0], 0.7))          # an empty run is the identity
+    o, lse = orc.merge_states(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    o_ref, lse_ref = orc.attention_rows(q, k, v, 0.7)
+    np.testing.assert_allclose(o, o_ref, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-13)
+
+
+def test_merge_all_empty_is_zero_and_ignores_garbage():
+    o_parts = np.full((3, 2, 4), np.nan)
+    lse_parts = np.full((3, 2), -np.inf)
+    o, lse = orc.merge_states(o_parts, lse_parts)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # an empty state with garbage output next to a real one leaves the real one unchanged
+    o_parts[0, 0] = [1, 2, 3, 4]
+    lse_parts[0, 0] = 0.5
+    o, lse = orc.merge_states(o_parts, lse_parts)
+    np.testing.assert_allclose(o[0], [1, 2, 3, 4])
+    assert lse[0] == 0.5
+
+
+def test_prefix_tail_merge_equals_full_attention_through_tables():
+    """Shared prefix read once, private tail per row, merged: equals decode over
+    the concatenated table (the n-sample path of the FMHA page)."""
+    rng = np.random.default_rng(13)
+    ps, hq, hkv, d = 4, 4, 2, 8
+    prefix_len, tails = 8, [3, 6, 1]
+    lk_p = rng.standard_normal((prefix_len, hkv, d))
+    lv_p = rng.standard_normal((prefix_len, hkv, d))
+    lk_t = [rng.standard_normal((t, hkv, d)) for t in tails]
+    lv_t = [rng.standard_normal((t, hkv, d)) for t in tails]
+    kp, vp, tab = _paged_pool_from_logical(rng, [lk_p] + lk_t, [lv_p] + lv_t, ps, 16)
+    n_pref_pages = prefix_len // ps
+    q = rng.standard_normal((len(tails), 1, hq, d)).astype(np.float32)
+    o_pre, l_pre = orc.attn_decode(kp, vp, q.reshape(1, len(tails), hq, d), tab[:1], [prefix_len], 0.3, "f32")
+    o_tail, l_tail = orc.attn_decode(kp, vp, q, tab[1:], tails, 0.3, "f32")
+    o, lse = orc.merge_states(np.stack([o_pre.reshape(len(tails), 1, hq, d), o_tail]),
+                              np.stack([l_pre.reshape(len(tails), 1, hq), l_tail]))
+    full = np.concatenate([np.repeat(tab[:1, :n_pref_pages], len(tails), 0), tab[1:]], axis=1)
+    o_full, lse_full = orc.attn_decode(kp, vp, q, full, [prefix_len + t for t in tails], 0.3, "f32")
+    np.testing.assert_allclose(o, o_full, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_full, atol=1e-13)

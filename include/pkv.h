@@ -1,0 +1,234 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged K/V cache on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (page titles and sections):
+ *   [P1] "Paged causal K/V cache and cached attention for VisualGen":
+ *        Description / Cache, Description / Attention, Per-File QA
+ *        Perspective, and the review thread on staged-token slot ids.
+ *   [P5] "Support shared-prefix attention for n-sample requests in FMHA":
+ *        commit messages on the FA4 prefix and tail passes, small-batch
+ *        splits, MIN_SPLIT_TOKENS and the grouping check.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All pointers except `pool` and the `pkv_pool` struct itself are DEVICE
+ *   pointers.  The caller owns every buffer; the library allocates no device
+ *   memory and keeps no state between calls.
+ * - Every call is asynchronous on `stream` and never synchronises with the
+ *   host, so a captured HIP graph replays it after the caller edits the
+ *   device-side lengths, tables or slots in place ([P1] Description / Cache,
+ *   graph-safety bullet).
+ * - Argument checks run on the host before anything is launched.  A failed
+ *   check returns a non-OK status, launches nothing and leaves every output
+ *   untouched.  Zero tokens / zero rows return PKV_OK with no launch.
+ * - Device-side contents are the caller's responsibility, as on the pages
+ *   ([P1] Per-File QA Perspective on scatterKvSlots): slots and page ids in
+ *   range, destination slots unique, kv_len <= the table row's capacity.
+ *   Violations are undefined behaviour.
+ * - Element strides and counts are in ELEMENTS of the stated dtype.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's own hipStream_t (a repeated identical typedef is legal). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  PKV_ERR_SHAPE = 2,       /* a size, stride or count is invalid                 */
+  PKV_ERR_DTYPE = 3,       /* a dtype argument is not one of pkv_dtype           */
+  PKV_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this combination          */
+  PKV_ERR_HIP = 5,         /* a kernel launch failed (hipGetLastError)           */
+  PKV_ERR_ALIGN = 6        /* a pointer or stride breaks the stated alignment    */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3FN = 2 /* OCP e4m3fn codes; real value = code value * scale */
+} pkv_dtype;
+
+/*
+ * A K/V page pool ([P1] Description / Cache: one pool and one page table,
+ * a page holds the same tokens in every layer; one layer's pool per call).
+ *
+ * Layout: K and V are separate pools.  Page p starts at `k + p * page_stride`
+ * (same stride for V) and holds [page_size, num_kv_heads, head_dim] elements,
+ * contiguous.  So pool slot s = p * page_size + r ([P1] slot-id review thread:
+ * int64 slot id = view_page * tokens_per_page + slot) is the row of
+ * num_kv_heads * head_dim elements at page s / page_size, row s % page_size.
+ * page_stride >= page_size * num_kv_heads * head_dim; a larger stride lets
+ * K and V pages interleave in one allocation.
+ *
+ * page_size is a power of two ([P1] review thread: the commit-time layout
+ * computes page and slot with shifts and masks).  The attention kernels need
+ * page_size >= 16; the scatter takes any power of two.
+ *
+ * dtype PKV_FP8_E4M3FN: k_scale / v_scale are float [num_pages, num_kv_heads]
+ * device arrays, the scale of each (page, kv head); NULL for other dtypes.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t page_stride;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pkv_dtype dtype;
+  const float* k_scale;
+  const float* v_scale;
+} pkv_pool;
+
+/* Text of a status code (static storage). */
+const char* pkv_status_string(pkv_status status);
+
+/* ABI version: bumps when a signature or layout changes. */
+int32_t pkv_abi_version(void);
+
+/*
+ * pkv_scatter_slots -- write new K/V token rows into pool slots.
+ * [P1] Description / Cache (chunk K/V write bullet) and Per-File QA
+ * Perspective on scatterKvSlots: the source is read once, with any token and
+ * head stride (so K/V slices of a packed QKV projection need no copy), and
+ * each token goes to one or two pool slots; optional source indices.
+ *
+ *   src_k, src_v       token i, kv head h starts at src + j * src_tok_stride
+ *                      + h * src_head_stride with j = src_idx ? src_idx[i] : i;
+ *                      head_dim elements contiguous; element type = pool dtype
+ *                      (the bytes are copied as they are: fp8 stays fp8).
+ *   src_idx            device int64 [n_tokens] or NULL.
+ *   slots              device int64 [n_tokens]; slot < 0 means skip.
+ *   slots2             device int64 [n_tokens] or NULL: second destination
+ *                      (slot < 0 means skip).
+ * Every (token, head) row is copied with the widest access (16, 8, 4, 2 or 1
+ * bytes) that the pointers and strides allow.  Duplicate destinations race
+ * (undefined which token wins).  fp8 scales are not touched.
+ * Errors: NULL pool/k/v/src/slots -> PKV_ERR_NULL; n_tokens < 0, bad pool
+ * geometry or strides -> PKV_ERR_SHAPE.
+ */
+pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void* src_v,
+                             int64_t src_tok_stride, int64_t src_head_stride,
+                             const int64_t* src_idx, const int64_t* slots, const int64_t* slots2,
+                             int64_t n_tokens, hipStream_t stream);
+
+/*
+ * pkv_attn_decode -- paged decode attention.
+ * [P1] Description / Attention (paged attention over block-table rows) and
+ * [P5] FA4 prefix / tail commit messages (n query rows share one table row:
+ * the shared-prefix pass of an n-sample group; natural-log LSE returned for
+ * the merge).
+ *
+ *   q            [num_tables, rows_per_table, num_q_heads, head_dim], q_dtype
+ *                PKV_BF16 (or PKV_F32), contiguous.
+ *   block_table  device int32 [num_tables, table_stride]: logical key p of
+ *                row t is slot block_table[t][p / page_size] * page_size +
+ *                p % page_size.  Entries at or past ceil(kv_lens[t] /
+ *                page_size) are never read ([P5] grouping commit).
+ *   kv_lens      device int32 [num_tables], 0 <= kv_lens[t] <= max_kv_len.
+ *   max_kv_len   host upper bound of kv_lens (plans the work split).
+ *   out          [num_tables, rows_per_table, num_q_heads, head_dim],
+ *                out_dtype PKV_F32 or PKV_BF16.
+ *   out_lse      NULL or float [num_tables, rows_per_table, num_q_heads]:
+ *                ln sum_k exp(sm_scale * q.k).
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).  A row with
+ * kv_lens = 0 gets out = 0 and lse = -inf.
+ *   workspace    NULL or device scratch of workspace_bytes (>= the value of
+ *                pkv_attn_decode_workspace_bytes for the same shapes) used for
+ *                cross-workgroup key splits and their merge.  With a NULL or
+ *                smaller workspace the call runs unsplit (same result up to
+ *                float rounding, possibly slower).
+ * Kernels: q bf16 with K/V bf16 or fp8 run on bf16 MFMA; q fp32 (any K/V
+ * dtype) runs on the vector ALUs.  head_dim 64 or 128.
+ * Errors: NULL pointers -> PKV_ERR_NULL; num_q_heads % num_kv_heads,
+ * negative sizes, page_size < 16 -> PKV_ERR_SHAPE; unknown dtype ->
+ * PKV_ERR_DTYPE; other head_dim / dtype combinations or missing fp8 scales ->
+ * PKV_ERR_UNSUPPORTED.
+ */
+size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_table, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len);
+
+pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                           int32_t num_tables, int32_t rows_per_table, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t table_stride, const int32_t* kv_lens,
+                           int32_t max_kv_len, float sm_scale,
+                           void* out, pkv_dtype out_dtype, float* out_lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_attn_prefill_block_causal -- paged prefill with causal blocks.
+ * [P1] Description / Cache (frame-causal attention needs no mask: the new
+ * tokens are cut into causal blocks, each with its own key count, full
+ * attention inside a block and causal across blocks; a block's new tokens are
+ * the last keys of its row) and Description / Attention (seq_len is the number
+ * of real query tokens; padding rows are neither written nor attended and
+ * their outputs are zero).
+ *
+ *   q                  query row i of batch b, head h starts at
+ *                      q + (b * s_q + i) * q_tok_stride + h * q_head_stride;
+ *                      head_dim contiguous (so q may be the Q slice of a packed
+ *                      [B, s_q, Hq + 2 Hkv, D] projection).  q_dtype PKV_BF16.
+ *   block_table        device int32 [batch, table_stride].
+ *   n_ctx, seq_len     device int32 [batch]: cached keys before the new tokens
+ *                      (pinned prefix + history) and real new tokens
+ *                      (<= s_q).  The new tokens must already sit at logical
+ *                      keys n_ctx .. n_ctx + seq_len - 1 of the table row.
+ *   causal_block_size  > 0: query i < seq_len of block i / cbs sees logical
+ *                      keys [0, n_ctx + min((i / cbs + 1) * cbs, seq_len));
+ *                      0: one block (every real query sees n_ctx + seq_len).
+ *   max_keys           host upper bound of n_ctx + seq_len.
+ *   out                [batch, s_q, num_q_heads, head_dim] contiguous,
+ *                      out_dtype PKV_BF16 or PKV_F32; rows i >= seq_len are 0.
+ *   out_lse            NULL or float [batch, s_q, num_q_heads]; -inf for
+ *                      padding rows.
+ *   workspace          NULL or scratch of pkv_attn_prefill_workspace_bytes
+ *                      (for key splits); NULL runs unsplit.
+ * Kernel: bf16 MFMA; K/V bf16; head_dim 128 or 64.
+ * Errors: as pkv_attn_decode.
+ */
+size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_keys);
+
+pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                         int64_t q_tok_stride, int64_t q_head_stride,
+                                         int32_t batch, int32_t s_q, int32_t num_q_heads,
+                                         const int32_t* block_table, int32_t table_stride,
+                                         const int32_t* n_ctx, const int32_t* seq_len,
+                                         int32_t causal_block_size, int32_t max_keys, float sm_scale,
+                                         void* out, pkv_dtype out_dtype, float* out_lse,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_merge_states -- join attention states over disjoint key sets.
+ * [P5] FA4 tail commit (prefix and tail states joined by one merge kernel,
+ * natural-log LSE) and small-batch split commit (an empty run has LSE -inf).
+ *
+ *   o_parts    float [num_states, rows, num_q_heads, head_dim], each state
+ *              normalised over its own keys.
+ *   lse_parts  float [num_states, rows, num_q_heads], natural log.
+ *   out        [rows, num_q_heads, head_dim], out_dtype PKV_F32 or PKV_BF16.
+ *   out_lse    NULL or float [rows, num_q_heads].
+ * With m = max_i lse_i, w_i = exp(lse_i - m): out = sum_i w_i o_i / sum_i w_i,
+ * lse = m + ln sum_i w_i.  If every lse_i is -inf: out = 0, lse = -inf, and
+ * no o_i is read.  States with weight 0 never contribute (NaN-safe).
+ * head_dim must be a multiple of 4.
+ * Errors: NULL -> PKV_ERR_NULL; num_states < 1 or bad sizes -> PKV_ERR_SHAPE.
+ */
+pkv_status pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t num_states, int64_t rows,
+                            int32_t num_q_heads, int32_t head_dim, void* out, pkv_dtype out_dtype,
+                            float* out_lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,201 @@
+"""Python binding of libpkv: paged K/V-cache attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the HIP kernels of
+``libpkv.so`` (built in-tree by ``paged_kv_cache_slots_amd.build``); if the
+library is missing, loading fails loudly.  Torch supplies device memory and
+the current stream; the C entry points take plain pointers and sizes.
+
+The functions carry the C names: ``pkv_scatter_slots``, ``pkv_attn_decode``,
+``pkv_attn_prefill_block_causal``, ``pkv_merge_states`` and the workspace
+size queries.  Any non-OK status raises :class:`PkvError`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
+                4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_HIP", 6: "PKV_ERR_ALIGN"}
+PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
+
+EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
+            "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
+            "pkv_merge_states"]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({text})")
+        self.status = status
+
+
+class PkvPoolStruct(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("page_stride", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libpkv.so is not built ({path}); run `python -m paged_kv_cache_slots_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    PP = ctypes.POINTER(PkvPoolStruct)
+    sig = {
+        "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkv_abi_version": (I32, []),
+        "pkv_scatter_slots": (ctypes.c_int, [PP, P, P, I64, I64, P, P, P, I64, P]),
+        "pkv_attn_decode_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "pkv_attn_decode": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
+                                           ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
+                                                         P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
+        "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != PKV_OK:
+        text = load_library().pkv_status_string(status).decode()
+        raise PkvError(fn, status, text)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PKV_F32
+    if t == torch.bfloat16:
+        return PKV_BF16
+    if t in (torch.float8_e4m3fn, torch.uint8):
+        return PKV_FP8_E4M3FN
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+@dataclass
+class Pool:
+    """A K/V page pool: ``k`` and ``v`` are ``[num_pages, page_size, Hkv, D]``
+    views (the page dimension may be strided); fp8 pools carry float scales
+    ``[num_pages, Hkv]``."""
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    def struct(self) -> PkvPoolStruct:
+        k, v = self.k, self.v
+        if k.shape != v.shape or k.dtype != v.dtype or k.stride() != v.stride():
+            raise ValueError("K and V pools must have the same shape, dtype and strides")
+        n, ps, hkv, d = k.shape
+        if k.stride()[1:] != (hkv * d, d, 1):
+            raise ValueError("each page must be contiguous [page_size, Hkv, D]")
+        return PkvPoolStruct(k.data_ptr(), v.data_ptr(), k.stride(0), n, ps, hkv, d, _dtype_code(k.dtype),
+                             _ptr(self.k_scale), _ptr(self.v_scale))
+
+
+def pkv_scatter_slots(pool: Pool, src_k: torch.Tensor, src_v: torch.Tensor, slots: torch.Tensor,
+                      src_idx: Optional[torch.Tensor] = None, slots2: Optional[torch.Tensor] = None,
+                      n_tokens: Optional[int] = None, stream=None) -> None:
+    """Write ``src_k/src_v`` token rows ([n_src, Hkv, D] views, any token and
+    head stride, D contiguous) into the pool at int64 ``slots`` (and
+    ``slots2``); negative slots are skipped."""
+    if src_k.stride() != src_v.stride() or src_k.stride(2) != 1:
+        raise ValueError("src_k and src_v must share strides with D contiguous")
+    n = slots.numel() if n_tokens is None else n_tokens
+    ps = pool.struct()
+    _check("pkv_scatter_slots", load_library().pkv_scatter_slots(
+        ctypes.byref(ps), src_k.data_ptr(), src_v.data_ptr(), src_k.stride(0), src_k.stride(1), _ptr(src_idx),
+        slots.data_ptr(), _ptr(slots2), n, _stream(stream)))
+
+
+def pkv_attn_decode_workspace_bytes(num_tables: int, rows_per_table: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, max_kv_len: int) -> int:
+    return int(load_library().pkv_attn_decode_workspace_bytes(num_tables, rows_per_table, num_q_heads,
+                                                              num_kv_heads, head_dim, max_kv_len))
+
+
+def pkv_attn_decode(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor, max_kv_len: int,
+                    sm_scale: float, out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Paged decode.  ``q`` is [T, n, Hq, D] contiguous; ``out`` likewise
+    (fp32 or bf16); ``out_lse`` [T, n, Hq] fp32 or None."""
+    if not q.is_contiguous() or not out.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q, out and block_table must be contiguous")
+    t, n, hq, _ = q.shape
+    ps = pool.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attn_decode", load_library().pkv_attn_decode(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
+        block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
+        _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_prefill_workspace_bytes(batch: int, s_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                     max_keys: int) -> int:
+    return int(load_library().pkv_attn_prefill_workspace_bytes(batch, s_q, num_q_heads, num_kv_heads, head_dim,
+                                                               max_keys))
+
+
+def pkv_attn_prefill_block_causal(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, n_ctx: torch.Tensor,
+                                  seq_len: torch.Tensor, causal_block_size: int, max_keys: int, sm_scale: float,
+                                  out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Block-causal prefill.  ``q`` is a [B, s_q, Hq, D] view whose rows are
+    ``q_tok_stride`` apart (batch rows consecutive) and heads
+    ``q_head_stride`` apart, D contiguous (a slice of a packed QKV works)."""
+    b, s_q, hq, d = q.shape
+    if q.stride(3) != 1 or (b > 1 and q.stride(0) != s_q * q.stride(1)):
+        raise ValueError("q rows must be evenly strided across the batch with D contiguous")
+    if not out.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("out and block_table must be contiguous")
+    ps = pool.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attn_prefill_block_causal", load_library().pkv_attn_prefill_block_causal(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), q.stride(1), q.stride(2), b, s_q, hq,
+        block_table.data_ptr(), block_table.stride(0), n_ctx.data_ptr(), seq_len.data_ptr(),
+        int(causal_block_size), int(max_keys), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype),
+        _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor,
+                     out_lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Merge ``o_parts`` [N, R, Hq, D] / ``lse_parts`` [N, R, Hq] (fp32,
+    contiguous) into ``out`` [R, Hq, D] (fp32 or bf16) and ``out_lse``."""
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous() and out.is_contiguous()):
+        raise ValueError("merge inputs and output must be contiguous")
+    n, r, hq, d = o_parts.shape
+    _check("pkv_merge_states", load_library().pkv_merge_states(
+        o_parts.data_ptr(), lse_parts.data_ptr(), n, r, hq, d, out.data_ptr(), _dtype_code(out.dtype),
+        _ptr(out_lse), _stream(stream)))

@@ -1,0 +1,578 @@
+// Paged decode attention.
+//
+// "Paged causal K/V cache and cached attention for VisualGen", Description /
+// Attention: attention over the keys a block-table row maps; "Support
+// shared-prefix attention for n-sample requests in FMHA", FA4 prefix / tail
+// commits: n query rows can share one table row (the shared-prefix pass of an
+// n-sample group), the result carries a natural-log LSE for the merge, and
+// the key range of a small grid is cut into splits joined by the LSE merge
+// (split-KV commits: only when it pays, chunks of at least 512 tokens).
+//
+// Work unit: (table row t, kv head g, key split s, row group).  The query rows
+// of a unit are R = rows_per_table * (Hq / Hkv) rows (sample i, head g*G + hh);
+// they share every K/V byte the unit reads, so K/V are read from HBM once per
+// unit.
+//
+// MFMA kernel (q bf16, K/V bf16 or fp8 e4m3fn):
+//   * A wave owns a block of 16 query rows.  The key range is walked in tiles
+//     of 32 logical keys = two 16-key halves, each inside one page (page_size
+//     >= 16).  Page ids of the next 64 tiles are fetched with one vector load
+//     and read back with readlane, so the table walk never stalls the loop.
+//   * S^T[key][row] = K Q^T on v_mfma_f32_16x16x32_bf16: the A operand is a
+//     key row (lane = key, 16-byte loads straight from the page), the B
+//     operand is Q held in registers for the whole kernel.  The output gives
+//     every lane one query row and 8 keys of the tile.
+//   * Online softmax per row in the log2 domain; the running max is shared by
+//     the four lanes of a row through two xor-shuffles.
+//   * O^T[dim][row] += V^T P^T on the same MFMA: P^T is the score registers
+//     converted to bf16 in place (no shuffle), V^T is built in registers from
+//     an 8-key x (D/16)-dim block that each lane loads directly (a 16-lane
+//     group reads whole 256-byte rows) and transposes with v_perm_b32.  The
+//     output row of a lane is its softmax row, so rescaling needs no shuffle.
+//   * fp8: codes are widened to bf16 exactly (v_cvt_pk_f32_fp8; an e4m3
+//     value fits bf16), the per-(page, kv head) K scale multiplies the scores
+//     and the V scale is folded into P before the PV product.
+//   * Dead rows of a partial last page and poison pages are selected away
+//     (scores to -inf, V rows to 0) before they can reach a product.
+//   * Waves of a workgroup either own different row blocks or split the
+//     tiles of one row block; split states are combined through LDS with the
+//     merge formula.  Cross-workgroup splits write normalised partial states
+//     and their LSE, joined by the merge kernel.
+//
+// VALU kernel (q fp32; any K/V dtype): one wave per (query row, split); the
+// exact fp32 path for small or fp32 problems.
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+
+// Pages of the 16-key halves of up to 64 consecutive tiles of one wave:
+// lane k holds the ids for tile `first + k * step`.
+struct PageWindow {
+  int32_t e0, e1;     // page of half 0 / half 1
+  float ks0, ks1;     // fp8 K scale of (page, kv head) for both halves
+  float vs0, vs1;
+};
+
+template <bool kFp8>
+__device__ __forceinline__ PageWindow fetch_pages(const DecodeParams& p, const int32_t* trow, int g, int first,
+                                                  int step, int te, int len) {
+  const int lane = threadIdx.x & 63;
+  const int tile = first + lane * step;
+  PageWindow w{0, 0, 1.f, 1.f, 1.f, 1.f};
+  if (tile < te) {
+    const int key0 = tile * 32;
+    w.e0 = trow[key0 >> p.page_shift];
+    w.e1 = (p.page_shift >= 5 || key0 + 16 >= len) ? w.e0 : trow[(key0 + 16) >> p.page_shift];
+    if constexpr (kFp8) {
+      w.ks0 = p.k_scale[(int64_t)w.e0 * p.num_kv_heads + g];
+      w.vs0 = p.v_scale[(int64_t)w.e0 * p.num_kv_heads + g];
+      w.ks1 = p.k_scale[(int64_t)w.e1 * p.num_kv_heads + g];
+      w.vs1 = p.v_scale[(int64_t)w.e1 * p.num_kv_heads + g];
+    }
+  }
+  return w;
+}
+
+__device__ __forceinline__ int rl(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+__device__ __forceinline__ float rlf(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+// Raw registers of one 32-key tile.
+template <int D, bool kFp8>
+struct TileRegs {
+  static constexpr int NCH = D / 32;                  // 32-dim MFMA chunks of QK
+  static constexpr int KLD = kFp8 ? NCH / 2 : NCH;    // 16-byte K loads per half
+  static constexpr int VB = kFp8 ? D / 16 : D / 8;    // bytes per V block row (D/16 dims)
+  u32x4 k[2][KLD];
+  // V: 8 keys x (D/16) dims; stored as dwords
+  uint32_t v[8][VB / 4 > 0 ? VB / 4 : 1];
+  int32_t page0, page1;
+  float ks0, ks1, vs0, vs1;
+};
+
+template <int D, bool kFp8>
+__device__ __forceinline__ void load_tile(TileRegs<D, kFp8>& r, const DecodeParams& p, int g, int page0,
+                                          int page1, int key0) {
+  using T = TileRegs<D, kFp8>;
+  const int lane = threadIdx.x & 63;
+  const int kk = lane & 15, j = lane >> 4;
+  constexpr int esz = kFp8 ? 1 : 2;
+  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
+  const int mask = (1 << p.page_shift) - 1;
+  const int row0 = key0 & mask;
+  const int row1 = (key0 + 16) & mask;
+  const int64_t base0 = (int64_t)page0 * p.page_stride + (int64_t)g * D;
+  const int64_t base1 = (int64_t)page1 * p.page_stride + (int64_t)g * D;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v_pool);
+  // K: lane = key kk of each half; chunk dims per lane group j
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t kb = (h == 0 ? base0 + (row0 + kk) * row_elems : base1 + (row1 + kk) * row_elems);
+#pragma unroll
+    for (int c = 0; c < T::KLD; ++c) {
+      const int dim = kFp8 ? (64 * c + 16 * j) : (32 * c + 8 * j);
+      r.k[h][c] = ld16(kp + (kb + dim) * esz);
+    }
+  }
+  // V: keys 4j..4j+3 of half 0 and of half 1, dims (D/16)*kk ..
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int h = t >> 2;
+    const int row = (h == 0 ? row0 : row1) + 4 * j + (t & 3);
+    const int64_t vb = (h == 0 ? base0 : base1) + row * row_elems + (D / 16) * kk;
+    const uint8_t* src = vp + vb * esz;
+    if constexpr (T::VB == 16) {
+      const u32x4 x = ld16(src);
+      r.v[t][0] = x[0]; r.v[t][1] = x[1]; r.v[t][2] = x[2]; r.v[t][3] = x[3];
+    } else if constexpr (T::VB == 8) {
+      const u32x2 x = ld8(src);
+      r.v[t][0] = x[0]; r.v[t][1] = x[1];
+    } else {
+      r.v[t][0] = *reinterpret_cast<const uint32_t*>(src);
+    }
+  }
+  r.page0 = page0;
+  r.page1 = page1;
+}
+
+// Running softmax state of one wave (16 rows, lane row = lane & 15).
+template <int D>
+struct RowState {
+  static constexpr int DPL = D / 16;
+  f32x4 o[DPL];   // O^T[dim DPL*(4j+i)+t'][row] in o[t'][i]
+  float m;        // running max (log2 domain), shared by the row's 4 lanes
+  float l;        // this lane's share of the running sum
+};
+
+template <int D, bool kFp8>
+__device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>& r, const u32x4 (&q)[D / 32],
+                                             float scale_log2, int key0, int len) {
+  using T = TileRegs<D, kFp8>;
+  constexpr int NCH = T::NCH;
+  constexpr int DPL = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int j = lane >> 4;
+
+  // ---- S^T = K Q^T for both 16-key halves
+  f32x4 s[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      u32x4 a;
+      if constexpr (kFp8) {
+        const u32x4 raw = r.k[h][i >> 1];
+        const int e = i & 1;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t dw = raw[2 * e + w];
+          const f32x2 f0 = fp8x2_to_f32<false>(dw);
+          const f32x2 f1 = fp8x2_to_f32<true>(dw);
+          a[2 * w] = pack_hi16(__float_as_uint(f0[0]), __float_as_uint(f0[1]));
+          a[2 * w + 1] = pack_hi16(__float_as_uint(f1[0]), __float_as_uint(f1[1]));
+        }
+      } else {
+        a = r.k[h][i];
+      }
+      acc = mfma16x16x32_bf16(a, q[i], acc);
+    }
+    s[h] = acc;
+  }
+  // ---- scale (and fp8 K scale), mask keys past the end
+  const float c0 = kFp8 ? scale_log2 * r.ks0 : scale_log2;
+  const float c1 = kFp8 ? scale_log2 * r.ks1 : scale_log2;
+  s[0] *= c0;
+  s[1] *= c1;
+  const bool partial = key0 + 32 > len;
+  if (partial) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 16 * h + 4 * j + i >= len) s[h][i] = kNegInf;
+  }
+  // ---- online softmax (row max shared by the 4 lanes of a row)
+  float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mt = wave_max_xor(mt, 16);
+  mt = wave_max_xor(mt, 32);
+  const float m_new = fmaxf(st.m, mt);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float pv[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(s[h][i] - m_use);
+      pv[4 * h + i] = e;
+      psum += e;
+    }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) st.o[t] *= alpha;
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] *= r.vs0;
+      pv[4 + i] *= r.vs1;
+    }
+  }
+  u32x4 pb;
+  pb[0] = pack_bf16x2(pv[0], pv[1]);
+  pb[1] = pack_bf16x2(pv[2], pv[3]);
+  pb[2] = pack_bf16x2(pv[4], pv[5]);
+  pb[3] = pack_bf16x2(pv[6], pv[7]);
+
+  // ---- V^T operands (8 keys of this lane group, one dim each); dead keys of
+  // a partial tile are zeroed in place first (0 * NaN would poison the sum)
+  constexpr int VW = T::VB / 4 > 0 ? T::VB / 4 : 1;   // raw dwords per key
+  if (partial) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bool ok = key0 + 16 * (t >> 2) + 4 * j + (t & 3) < len;
+#pragma unroll
+      for (int w = 0; w < VW; ++w) r.v[t][w] = ok ? r.v[t][w] : 0u;
+    }
+  }
+  if constexpr (!kFp8) {
+    // dword w of key t holds dims 2w (low half) and 2w+1 (high half)
+#pragma unroll
+    for (int tp = 0; tp < DPL; ++tp) {
+      const int w = tp >> 1;
+      u32x4 a;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+        a[q2] = (tp & 1) ? pack_hi16(r.v[2 * q2][w], r.v[2 * q2 + 1][w])
+                         : pack_lo16(r.v[2 * q2][w], r.v[2 * q2 + 1][w]);
+      st.o[tp] = mfma16x16x32_bf16(a, pb, st.o[tp]);
+    }
+  } else {
+    // fp8: for dims (tp, tp+1) gather the codes of keys (2q, 2q+1) into one
+    // dword [k0.tp, k1.tp, k0.tp+1, k1.tp+1], widen each half to two floats and
+    // keep their high halves (exact bf16)
+#pragma unroll
+    for (int tp = 0; tp < DPL; tp += 2) {
+      const int w = tp >> 2;
+      const uint32_t sel = (tp & 2) ? 0x07030602u : 0x05010400u;
+      u32x4 a0, a1;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t mixed = perm_b32(r.v[2 * q2 + 1][w], r.v[2 * q2][w], sel);
+        const f32x2 lo = fp8x2_to_f32<false>(mixed);
+        const f32x2 hi = fp8x2_to_f32<true>(mixed);
+        a0[q2] = pack_hi16(__float_as_uint(lo[0]), __float_as_uint(lo[1]));
+        a1[q2] = pack_hi16(__float_as_uint(hi[0]), __float_as_uint(hi[1]));
+      }
+      st.o[tp] = mfma16x16x32_bf16(a0, pb, st.o[tp]);
+      st.o[tp + 1] = mfma16x16x32_bf16(a1, pb, st.o[tp + 1]);
+    }
+  }
+}
+
+}  // namespace
+
+template <int D, bool kFp8, int WP>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int WR = 4 / WP;
+  constexpr int NCH = D / 32;
+  constexpr int DPL = D / 16;
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const int n_rg = gridDim.z / p.num_tables;
+  const int t = blockIdx.z / n_rg;
+  const int rg = blockIdx.z - t * n_rg;
+  const int wave = threadIdx.x >> 6;
+  const int wr = wave / WP, wp = wave - (wave / WP) * WP;
+  const int lane = threadIdx.x & 63;
+  const int r_lane = lane & 15, j = lane >> 4;
+  const int R = p.rows_per_table * p.group;
+  const int rb = rg * WR + wr;
+
+  const int len = p.kv_lens[t];
+  const int tiles = (len + 31) >> 5;
+  const int tb = s * p.tiles_per_split;
+  int te = tb + p.tiles_per_split;
+  te = te < tiles ? te : tiles;
+  if (p.splits > 1 && tb >= te) return;   // empty split: the merge never reads it
+
+  // ---- this lane's query row and its Q operand chunks
+  const int r = rb * 16 + r_lane;
+  const bool row_ok = r < R;
+  const int qi = row_ok ? r / p.group : 0;
+  const int qh = g * p.group + (row_ok ? r - qi * p.group : 0);
+  const int64_t qrow = ((int64_t)t * p.rows_per_table + qi) * p.num_q_heads + qh;
+  u32x4 q[NCH];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int dim = kFp8 ? (64 * (i >> 1) + 16 * j + 8 * (i & 1)) : (32 * i + 8 * j);
+      q[i] = row_ok ? ld16(qp + dim) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  RowState<D> st;
+#pragma unroll
+  for (int tp = 0; tp < DPL; ++tp) st.o[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
+
+  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  const int first = tb + wp;
+  const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
+  if (rb * 16 < R && n_mine > 0) {
+    TileRegs<D, kFp8> A, B;
+    PageWindow win = fetch_pages<kFp8>(p, trow, g, first, WP, te, len);
+    // Load the registers of the wave's it-th tile; page ids come from the
+    // window, refreshed every 64 tiles.
+    auto prep = [&](TileRegs<D, kFp8>& X, int it) {
+      const int k = it & 63;
+      if (k == 0 && it > 0) win = fetch_pages<kFp8>(p, trow, g, first + it * WP, WP, te, len);
+      load_tile<D, kFp8>(X, p, g, rl(win.e0, k), rl(win.e1, k), (first + it * WP) * 32);
+      if constexpr (kFp8) {
+        X.ks0 = rlf(win.ks0, k);
+        X.ks1 = rlf(win.ks1, k);
+        X.vs0 = rlf(win.vs0, k);
+        X.vs1 = rlf(win.vs1, k);
+      }
+    };
+    // two register sets: the next tile is in flight while this one computes
+    prep(A, 0);
+    for (int it = 0; it < n_mine; it += 2) {
+      if (it + 1 < n_mine) prep(B, it + 1);
+      compute_tile<D, kFp8>(st, A, q, p.scale_log2, (first + it * WP) * 32, len);
+      if (it + 1 >= n_mine) break;
+      if (it + 2 < n_mine) prep(A, it + 2);
+      compute_tile<D, kFp8>(st, B, q, p.scale_log2, (first + (it + 1) * WP) * 32, len);
+    }
+  }
+
+  // ---- full row sum of this wave
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
+
+  // ---- combine the WP tile-split waves of each row block through LDS
+  if constexpr (WP > 1) {
+    __shared__ float sm_ml[4][2][16];
+    __shared__ f32x4 sm_o[4][64][DPL];
+    if (j == 0) {
+      sm_ml[wave][0][r_lane] = st.m;
+      sm_ml[wave][1][r_lane] = st.l;
+    }
+#pragma unroll
+    for (int tp = 0; tp < DPL; ++tp) sm_o[wave][lane][tp] = st.o[tp];
+    __syncthreads();
+    if (wp != 0) return;
+    float m_all = kNegInf;
+#pragma unroll
+    for (int w = 0; w < WP; ++w) m_all = fmaxf(m_all, sm_ml[wave + w][0][r_lane]);
+    const float m_use = m_all == kNegInf ? 0.f : m_all;
+    float l_all = 0.f;
+    f32x4 o_all[DPL];
+#pragma unroll
+    for (int tp = 0; tp < DPL; ++tp) o_all[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < WP; ++w) {
+      const float f = fast_exp2(sm_ml[wave + w][0][r_lane] - m_use);
+      l_all += f * sm_ml[wave + w][1][r_lane];
+#pragma unroll
+      for (int tp = 0; tp < DPL; ++tp) o_all[tp] += f * sm_o[wave + w][lane][tp];
+    }
+    st.m = m_all;
+    st.l = l_all;
+#pragma unroll
+    for (int tp = 0; tp < DPL; ++tp) st.o[tp] = o_all[tp];
+  }
+  if (!row_ok) return;
+
+  // ---- normalise and store: this lane holds dims DPL*(4j+i) + t' of its row
+  const bool empty = st.l == 0.f;
+  const float inv = empty ? 0.f : 1.0f / st.l;
+  const float lse = empty ? kNegInf : (st.m + fast_log2(st.l)) * kLn2;
+  if (p.splits == 1) {
+    if (p.out_bf16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + qrow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w[DPL / 2];
+#pragma unroll
+        for (int tp = 0; tp < DPL; tp += 2) w[tp / 2] = pack_bf16x2(st.o[tp][i] * inv, st.o[tp + 1][i] * inv);
+        uint16_t* dst = o + DPL * (4 * j + i);
+        if constexpr (DPL == 8) *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+      }
+    } else {
+      float* o = reinterpret_cast<float*>(p.out) + qrow * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int tp = 0; tp < DPL; tp += 4)
+          *reinterpret_cast<f32x4*>(o + DPL * (4 * j + i) + tp) =
+              f32x4{st.o[tp][i] * inv, st.o[tp + 1][i] * inv, st.o[tp + 2][i] * inv, st.o[tp + 3][i] * inv};
+    }
+    if (p.out_lse && j == 0) p.out_lse[qrow] = lse;
+  } else {
+    const int64_t plane = (int64_t)p.num_tables * p.rows_per_table * p.num_q_heads;
+    float* o = p.ws_o + ((int64_t)s * plane + qrow) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tp = 0; tp < DPL; tp += 4)
+        *reinterpret_cast<f32x4*>(o + DPL * (4 * j + i) + tp) =
+            f32x4{st.o[tp][i] * inv, st.o[tp + 1][i] * inv, st.o[tp + 2][i] * inv, st.o[tp + 3][i] * inv};
+    if (j == 0) p.ws_lse[(int64_t)s * plane + qrow] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU kernel: one wave per (query row, split), fp32 arithmetic throughout.
+// ---------------------------------------------------------------------------
+
+template <int KV>
+__device__ __forceinline__ float load_kv(const void* pool, int64_t idx) {
+  if constexpr (KV == kF32) return reinterpret_cast<const float*>(pool)[idx];
+  else if constexpr (KV == kBF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(pool)[idx]);
+  else return fp8x2_to_f32<false>(reinterpret_cast<const uint8_t*>(pool)[idx])[0];
+}
+
+template <int D, int QT, int KV>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
+  constexpr int DPT = D / 64;   // dims per lane in the PV product
+  const int s = blockIdx.x;
+  const int64_t qrow = blockIdx.y;   // (t * n + i) * Hq + h
+  const int h = (int)(qrow % p.num_q_heads);
+  const int t = (int)(qrow / ((int64_t)p.num_q_heads * p.rows_per_table));
+  const int g = h / p.group;
+  const int lane = threadIdx.x;
+  const int len = p.kv_lens[t];
+  const int tiles = (len + 31) >> 5;
+  const int tb = s * p.tiles_per_split;
+  int te = tb + p.tiles_per_split;
+  te = te < tiles ? te : tiles;
+  if (p.splits > 1 && tb >= te) return;
+  const int kb = tb * 32;
+  const int ke = min(te * 32, len);
+
+  __shared__ float qs[D];
+  for (int d = lane; d < D; d += 64) {
+    if constexpr (QT == kF32) qs[d] = reinterpret_cast<const float*>(p.q)[qrow * D + d];
+    else qs[d] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qrow * D + d]);
+  }
+  __syncthreads();
+
+  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  const int mask = (1 << p.page_shift) - 1;
+  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
+  float m = kNegInf, l = 0.f;
+  float o[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) o[e] = 0.f;
+
+  for (int key0 = kb; key0 < ke; key0 += 64) {
+    const int key = key0 + lane;
+    float sc = kNegInf;
+    int64_t kbase = 0;
+    float kscale = 1.f;
+    if (key < ke) {
+      const int page = trow[key >> p.page_shift];
+      kbase = (int64_t)page * p.page_stride + (int64_t)(key & mask) * row_elems + (int64_t)g * D;
+      if constexpr (KV == kFP8) kscale = p.k_scale[(int64_t)page * p.num_kv_heads + g];
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qs[d], load_kv<KV>(p.k_pool, kbase + d), acc);
+      sc = acc * kscale * p.scale_log2;
+    }
+    float mt = sc;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) mt = wave_max_xor(mt, x);
+    const float m_new = fmaxf(m, mt);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    const float pk = fast_exp2(sc - m_use);
+    float ps = pk;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) ps = wave_sum_xor(ps, x);
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) o[e] *= alpha;
+    const int n_here = min(64, ke - key0);
+    for (int kk = 0; kk < n_here; ++kk) {
+      const float pj = __shfl(pk, kk, 64);
+      const int kj = key0 + kk;
+      const int page = trow[kj >> p.page_shift];
+      float vscale = 1.f;
+      if constexpr (KV == kFP8) vscale = p.v_scale[(int64_t)page * p.num_kv_heads + g];
+      const int64_t vbase = (int64_t)page * p.page_stride + (int64_t)(kj & mask) * row_elems + (int64_t)g * D;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) o[e] = fmaf(pj * vscale, load_kv<KV>(p.v_pool, vbase + lane + 64 * e), o[e]);
+    }
+  }
+  const bool empty = l == 0.f;
+  const float inv = empty ? 0.f : 1.0f / l;
+  const float lse = empty ? kNegInf : (m + fast_log2(l)) * kLn2;
+  if (p.splits == 1) {
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const int64_t idx = qrow * D + lane + 64 * e;
+      if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[idx] = f32_to_bf16_bits(o[e] * inv);
+      else reinterpret_cast<float*>(p.out)[idx] = o[e] * inv;
+    }
+    if (p.out_lse && lane == 0) p.out_lse[qrow] = lse;
+  } else {
+    const int64_t plane = (int64_t)p.num_tables * p.rows_per_table * p.num_q_heads;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) p.ws_o[((int64_t)s * plane + qrow) * D + lane + 64 * e] = o[e] * inv;
+    if (lane == 0) p.ws_lse[(int64_t)s * plane + qrow] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <int D, bool kFp8>
+static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
+  const int R = p.rows_per_table * p.group;
+  const int blocks16 = (R + 15) / 16;
+  const dim3 block(256);
+  if (blocks16 <= 1) {
+    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 4>), grid, block, 0, stream, p);
+  } else if (blocks16 <= 2) {
+    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 2>), grid, block, 0, stream, p);
+  } else {
+    const int rg = (blocks16 + 3) / 4;
+    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables * rg);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 1>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return kv == kFP8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
+  return kv == kFP8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
+}
+
+template <int D, int QT>
+static hipError_t launch_valu_dq(const DecodeParams& p, ElemType kv, hipStream_t stream) {
+  const dim3 grid(p.splits, (unsigned)((int64_t)p.num_tables * p.rows_per_table * p.num_q_heads)), block(64);
+  if (kv == kF32) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kF32>), grid, block, 0, stream, p);
+  else if (kv == kBF16) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kBF16>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_valu_kernel<D, QT, kFP8>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return q == kF32 ? launch_valu_dq<128, kF32>(p, kv, stream) : launch_valu_dq<128, kBF16>(p, kv, stream);
+  return q == kF32 ? launch_valu_dq<64, kF32>(p, kv, stream) : launch_valu_dq<64, kBF16>(p, kv, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,303 @@
+// Host side of the libpkv C ABI: argument checks (before any HIP call), work
+// planning and kernel dispatch.  No device memory is allocated here and no
+// host synchronisation happens; see include/pkv.h for the contract.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.hpp"
+
+namespace {
+
+using namespace pkv;
+
+constexpr int kAbiVersion = 1;
+
+// Key splits of the decode: chunks of at least 512 tokens and at most 16
+// splits ("Support shared-prefix attention for n-sample requests in FMHA",
+// split-KV and MIN_SPLIT_TOKENS commit messages).  The split count depends on
+// host arguments only, so the workspace size is known before the call.
+constexpr int kMinSplitTokens = 512;
+constexpr int kMaxSplits = 16;
+
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3FN; }
+int elem_bytes(pkv_dtype d) { return d == PKV_F32 ? 4 : d == PKV_BF16 ? 2 : 1; }
+ElemType elem_type(pkv_dtype d) { return d == PKV_F32 ? kF32 : d == PKV_BF16 ? kBF16 : kFP8; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pkv_status check_pool(const pkv_pool* pool) {
+  if (!pool || !pool->k || !pool->v) return PKV_ERR_NULL;
+  if (!valid_dtype(pool->dtype)) return PKV_ERR_DTYPE;
+  if (pool->num_pages < 1 || pool->num_kv_heads < 1 || pool->head_dim < 1) return PKV_ERR_SHAPE;
+  if (!is_pow2(pool->page_size)) return PKV_ERR_SHAPE;
+  if (pool->page_stride < (int64_t)pool->page_size * pool->num_kv_heads * pool->head_dim) return PKV_ERR_SHAPE;
+  if (pool->dtype == PKV_FP8_E4M3FN && (!pool->k_scale || !pool->v_scale)) return PKV_ERR_NULL;
+  return PKV_OK;
+}
+
+struct SplitPlan {
+  int splits;
+  int tiles_per_split;
+};
+
+SplitPlan plan_decode(int32_t max_kv_len) {
+  const int64_t tiles = std::max<int64_t>(1, ceil_div(std::max(max_kv_len, 0), 32));
+  const int64_t by_len = ceil_div(std::max(max_kv_len, 1), kMinSplitTokens);
+  const int splits = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, by_len));
+  return SplitPlan{splits, (int)ceil_div(tiles, splits)};
+}
+
+size_t decode_ws_bytes(int64_t rows, int32_t num_q_heads, int32_t head_dim, int splits) {
+  if (splits <= 1) return 0;
+  const int64_t plane = rows * num_q_heads;
+  return (size_t)(splits * plane * (int64_t)(head_dim + 1) * (int64_t)sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid size, stride or count";
+    case PKV_ERR_DTYPE: return "unknown dtype";
+    case PKV_ERR_UNSUPPORTED: return "no kernel for this head_dim / dtype / page_size combination";
+    case PKV_ERR_HIP: return "kernel launch failed";
+    case PKV_ERR_ALIGN: return "pointer or stride breaks the required alignment";
+  }
+  return "unknown status";
+}
+
+int32_t pkv_abi_version(void) { return kAbiVersion; }
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void* src_v, int64_t src_tok_stride,
+                             int64_t src_head_stride, const int64_t* src_idx, const int64_t* slots,
+                             const int64_t* slots2, int64_t n_tokens, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (n_tokens < 0 || src_tok_stride < 0 || src_head_stride < 0) return PKV_ERR_SHAPE;
+  if (n_tokens == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!src_k || !src_v || !slots) return PKV_ERR_NULL;
+  const int es = elem_bytes(pool->dtype);
+  const int64_t row_b = (int64_t)pool->head_dim * es;
+  int vec = 16;
+  while (vec > 1) {
+    const bool ok = row_b % vec == 0 && aligned(src_k, vec) && aligned(src_v, vec) && aligned(pool->k, vec) &&
+                    aligned(pool->v, vec) && (src_tok_stride * es) % vec == 0 &&
+                    (src_head_stride * es) % vec == 0 && (pool->page_stride * es) % vec == 0;
+    if (ok) break;
+    vec >>= 1;
+  }
+  ScatterParams p;
+  p.src_k = static_cast<const uint8_t*>(src_k);
+  p.src_v = static_cast<const uint8_t*>(src_v);
+  p.pool_k = static_cast<uint8_t*>(pool->k);
+  p.pool_v = static_cast<uint8_t*>(pool->v);
+  p.src_idx = src_idx;
+  p.slots = slots;
+  p.slots2 = slots2;
+  p.n_tokens = n_tokens;
+  p.src_tok_stride_b = src_tok_stride * es;
+  p.src_head_stride_b = src_head_stride * es;
+  p.page_stride_b = pool->page_stride * es;
+  p.row_stride_b = (int64_t)pool->num_kv_heads * row_b;
+  p.page_shift = log2i(pool->page_size);
+  p.num_kv_heads = pool->num_kv_heads;
+  p.vecs_per_row = (int32_t)(row_b / vec);
+  return launch_scatter(p, vec, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_table, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_kv_len) {
+  (void)num_kv_heads;
+  if (num_tables <= 0 || rows_per_table <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const SplitPlan plan = plan_decode(max_kv_len);
+  return decode_ws_bytes((int64_t)num_tables * rows_per_table, num_q_heads, head_dim, plan.splits);
+}
+
+pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
+                           int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
+                           int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                           void* out, pkv_dtype out_dtype, float* out_lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+  if (num_tables < 0 || rows_per_table < 1 || num_q_heads < 1 || table_stride < 1 || max_kv_len < 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_kv_len > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;
+  if (num_tables == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!q || !block_table || !kv_lens || !out) return PKV_ERR_NULL;
+  const int D = pool->head_dim;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype == PKV_FP8_E4M3FN || out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  const bool use_mfma = q_dtype == PKV_BF16 && pool->dtype != PKV_F32;
+  const int es = elem_bytes(pool->dtype);
+  if (use_mfma) {
+    if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * es) % 16 != 0 || !aligned(q, 16) ||
+        !aligned(out, 16))
+      return PKV_ERR_ALIGN;
+  } else if (!aligned(q, elem_bytes(q_dtype)) || !aligned(out, elem_bytes(out_dtype)) ||
+             !aligned(pool->k, es) || !aligned(pool->v, es)) {
+    return PKV_ERR_ALIGN;
+  }
+
+  const int64_t rows = (int64_t)num_tables * rows_per_table;
+  SplitPlan plan = plan_decode(max_kv_len);
+  const size_t need = decode_ws_bytes(rows, num_q_heads, D, plan.splits);
+  if (plan.splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) {
+    plan.splits = 1;
+    plan.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(max_kv_len, 32));
+  }
+
+  DecodeParams p;
+  p.k_pool = pool->k;
+  p.v_pool = pool->v;
+  p.k_scale = pool->k_scale;
+  p.v_scale = pool->v_scale;
+  p.q = q;
+  p.table = block_table;
+  p.kv_lens = kv_lens;
+  p.out = out;
+  p.out_lse = out_lse;
+  p.ws_o = nullptr;
+  p.ws_lse = nullptr;
+  if (plan.splits > 1) {
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + (int64_t)plan.splits * rows * num_q_heads * D;
+  }
+  p.page_stride = pool->page_stride;
+  p.page_shift = log2i(pool->page_size);
+  p.num_kv_heads = pool->num_kv_heads;
+  p.num_tables = num_tables;
+  p.rows_per_table = rows_per_table;
+  p.num_q_heads = num_q_heads;
+  p.group = num_q_heads / pool->num_kv_heads;
+  p.table_stride = table_stride;
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.out_bf16 = out_dtype == PKV_BF16;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+
+  hipError_t e = use_mfma ? launch_decode_mfma(p, elem_type(pool->dtype), D, stream)
+                          : launch_decode_valu(p, elem_type(q_dtype), elem_type(pool->dtype), D, stream);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  if (plan.splits > 1) {
+    MergeParams m;
+    m.o_parts = p.ws_o;
+    m.lse_parts = p.ws_lse;
+    m.out = out;
+    m.out_lse = out_lse;
+    m.kv_lens = kv_lens;
+    m.rows = rows;
+    m.num_states = plan.splits;
+    m.num_q_heads = num_q_heads;
+    m.head_dim = D;
+    m.rows_per_table = rows_per_table;
+    m.keys_per_state = plan.tiles_per_split * 32;
+    m.out_bf16 = out_dtype == PKV_BF16;
+    if (launch_merge(m, stream) != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_keys) {
+  (void)batch; (void)s_q; (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)max_keys;
+  return 0;
+}
+
+pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                         int64_t q_tok_stride, int64_t q_head_stride, int32_t batch, int32_t s_q,
+                                         int32_t num_q_heads, const int32_t* block_table, int32_t table_stride,
+                                         const int32_t* n_ctx, const int32_t* seq_len, int32_t causal_block_size,
+                                         int32_t max_keys, float sm_scale, void* out, pkv_dtype out_dtype,
+                                         float* out_lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  (void)workspace; (void)workspace_bytes;
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+  if (batch < 0 || s_q < 0 || num_q_heads < 1 || table_stride < 1 || max_keys < 0 || causal_block_size < 0 ||
+      q_tok_stride < 0 || q_head_stride < 0)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_keys > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;
+  if (batch == 0 || s_q == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!q || !block_table || !n_ctx || !seq_len || !out) return PKV_ERR_NULL;
+  const int D = pool->head_dim;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype != PKV_BF16 || pool->dtype != PKV_BF16 || out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * 2) % 16 != 0 || !aligned(q, 16) ||
+      (q_tok_stride * 2) % 16 != 0 || (q_head_stride * 2) % 16 != 0 || !aligned(out, 16))
+    return PKV_ERR_ALIGN;
+
+  PrefillParams p;
+  p.k_pool = pool->k;
+  p.v_pool = pool->v;
+  p.q = static_cast<const uint16_t*>(q);
+  p.table = block_table;
+  p.n_ctx = n_ctx;
+  p.seq_len = seq_len;
+  p.out = out;
+  p.out_lse = out_lse;
+  p.page_stride = pool->page_stride;
+  p.q_tok_stride = q_tok_stride;
+  p.q_head_stride = q_head_stride;
+  p.page_shift = log2i(pool->page_size);
+  p.num_kv_heads = pool->num_kv_heads;
+  p.batch = batch;
+  p.s_q = s_q;
+  p.num_q_heads = num_q_heads;
+  p.group = num_q_heads / pool->num_kv_heads;
+  p.table_stride = table_stride;
+  p.causal_block_size = causal_block_size;
+  p.q_tiles = 0;
+  p.out_bf16 = out_dtype == PKV_BF16;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return launch_prefill_mfma(p, D, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t num_states, int64_t rows,
+                            int32_t num_q_heads, int32_t head_dim, void* out, pkv_dtype out_dtype, float* out_lse,
+                            hipStream_t stream) {
+  if (!valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+  if (num_states < 1 || rows < 0 || num_q_heads < 1 || head_dim < 4 || head_dim % 4 != 0) return PKV_ERR_SHAPE;
+  if (out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  if (rows == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!o_parts || !lse_parts || !out) return PKV_ERR_NULL;
+  if (!aligned(o_parts, 16) || !aligned(out, out_dtype == PKV_F32 ? 16 : 8)) return PKV_ERR_ALIGN;
+  MergeParams m;
+  m.o_parts = o_parts;
+  m.lse_parts = lse_parts;
+  m.out = out;
+  m.out_lse = out_lse;
+  m.kv_lens = nullptr;
+  m.rows = rows;
+  m.num_states = num_states;
+  m.num_q_heads = num_q_heads;
+  m.head_dim = head_dim;
+  m.rows_per_table = 1;
+  m.keys_per_state = 1;
+  m.out_bf16 = out_dtype == PKV_BF16;
+  return launch_merge(m, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

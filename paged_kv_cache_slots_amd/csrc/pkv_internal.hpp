@@ -1,0 +1,107 @@
+// Internal launch parameters and launchers of libpkv.  Host code validates the
+// public arguments (pkv_api.cpp) and then fills these plain structs, which the
+// kernels take by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+enum ElemType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct ScatterParams {
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* pool_k;
+  uint8_t* pool_v;
+  const int64_t* src_idx;   // nullable
+  const int64_t* slots;
+  const int64_t* slots2;    // nullable
+  int64_t n_tokens;
+  int64_t src_tok_stride_b;   // bytes
+  int64_t src_head_stride_b;  // bytes
+  int64_t page_stride_b;      // bytes
+  int64_t row_stride_b;       // bytes between pool rows of one page (= Hkv * D * esize)
+  int32_t page_shift;         // log2(page_size)
+  int32_t num_kv_heads;
+  int32_t vecs_per_row;       // head_dim * esize / vec_bytes
+};
+
+// One decode problem: rows (t, i, h) of q attend to the first kv_lens[t] logical keys of table row t.
+struct DecodeParams {
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;       // fp8 only
+  const float* v_scale;
+  const void* q;
+  const int32_t* table;
+  const int32_t* kv_lens;
+  void* out;
+  float* out_lse;             // nullable
+  float* ws_o;                // [splits, T, n, Hq, D] when splits > 1
+  float* ws_lse;              // [splits, T, n, Hq]
+  int64_t page_stride;        // elements
+  int32_t page_shift;
+  int32_t num_kv_heads;
+  int32_t num_tables;
+  int32_t rows_per_table;     // n
+  int32_t num_q_heads;
+  int32_t group;              // Hq / Hkv
+  int32_t table_stride;
+  int32_t splits;             // cross-workgroup key splits
+  int32_t tiles_per_split;    // 32-key tiles per split
+  int32_t out_bf16;
+  float scale_log2;           // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* o_parts;       // [N, rows, Hq, D]
+  const float* lse_parts;     // [N, rows, Hq]
+  void* out;
+  float* out_lse;             // nullable
+  const int32_t* kv_lens;     // nullable: decode-split mode (valid states per table row)
+  int64_t rows;
+  int32_t num_states;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t rows_per_table;     // decode-split mode: rows per table row
+  int32_t keys_per_state;     // decode-split mode: keys covered by one state
+  int32_t out_bf16;
+};
+
+struct PrefillParams {
+  const void* k_pool;
+  const void* v_pool;
+  const uint16_t* q;          // bf16
+  const int32_t* table;
+  const int32_t* n_ctx;
+  const int32_t* seq_len;
+  void* out;
+  float* out_lse;
+  int64_t page_stride;
+  int64_t q_tok_stride;
+  int64_t q_head_stride;
+  int32_t page_shift;
+  int32_t num_kv_heads;
+  int32_t batch;
+  int32_t s_q;
+  int32_t num_q_heads;
+  int32_t group;
+  int32_t table_stride;
+  int32_t causal_block_size;
+  int32_t q_tiles;            // ceil(s_q / q tile rows)
+  int32_t out_bf16;
+  float scale_log2;
+};
+
+// Launchers: return hipGetLastError() of their launch.
+hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace pkv

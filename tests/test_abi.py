@@ -1,0 +1,121 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/pkv.h
+declares, and refuses bad arguments on the host before any HIP call (so these
+tests need no GPU; no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_slots_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000      # a fake 64 KiB-aligned device address: never dereferenced by the host checks
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\**(pkv_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.load_library()
+    names = _declared()
+    assert set(names) == set(pkv.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = pkv.load_library()
+    assert lib.pkv_abi_version() == 1
+    for code in range(7):
+        assert lib.pkv_status_string(code)
+
+
+def _pool(**kw):
+    d = dict(k=A, v=2 * A, page_stride=32 * 8 * 128, num_pages=100, page_size=32, num_kv_heads=8, head_dim=128,
+             dtype=pkv.PKV_BF16, k_scale=None, v_scale=None)
+    d.update(kw)
+    return pkv.PkvPoolStruct(**d)
+
+
+def _decode(pool, **kw):
+    a = dict(q=A, q_dtype=pkv.PKV_BF16, T=4, n=1, hq=32, table=A, tstride=128, lens=A, maxlen=4096, scale=0.1,
+             out=A, out_dtype=pkv.PKV_BF16, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return pkv.load_library().pkv_attn_decode(ctypes.byref(pool), a["q"], a["q_dtype"], a["T"], a["n"], a["hq"],
+                                              a["table"], a["tstride"], a["lens"], a["maxlen"], a["scale"],
+                                              a["out"], a["out_dtype"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("pool_kw,call_kw,expect", [
+    ({"k": None}, {}, 1),
+    ({}, {"q": None}, 1),
+    ({}, {"lens": None}, 1),
+    ({"dtype": pkv.PKV_FP8_E4M3FN}, {}, 1),                 # fp8 without scales
+    ({"page_size": 24}, {}, 2),                             # not a power of two
+    ({}, {"hq": 30}, 2),                                    # Hq % Hkv != 0
+    ({}, {"maxlen": 128 * 32 + 1}, 2),                      # beyond the table's capacity
+    ({"page_stride": 100}, {}, 2),
+    ({}, {"q_dtype": 7}, 3),
+    ({"head_dim": 96, "page_stride": 32 * 8 * 96}, {}, 4),
+    ({"page_size": 8}, {"tstride": 1024}, 4),
+    ({}, {"out_dtype": pkv.PKV_FP8_E4M3FN}, 4),
+    ({"k": A + 2}, {}, 6),
+    ({}, {"T": 0}, 0),                                      # empty batch: OK, nothing launched
+])
+def test_decode_argument_checks(pool_kw, call_kw, expect):
+    assert _decode(_pool(**pool_kw), **call_kw) == expect
+
+
+def test_scatter_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+    assert lib.pkv_scatter_slots(ctypes.byref(p), None, A, 0, 0, None, A, None, 4, None) == 1
+    assert lib.pkv_scatter_slots(ctypes.byref(p), A, A, 0, 0, None, None, None, 4, None) == 1
+    assert lib.pkv_scatter_slots(ctypes.byref(p), A, A, 0, 0, None, A, None, -1, None) == 2
+    assert lib.pkv_scatter_slots(ctypes.byref(p), A, A, -5, 0, None, A, None, 4, None) == 2
+    assert lib.pkv_scatter_slots(ctypes.byref(p), A, A, 1024, 128, None, A, None, 0, None) == 0
+    bad = _pool(page_size=48)
+    assert lib.pkv_scatter_slots(ctypes.byref(bad), A, A, 1024, 128, None, A, None, 4, None) == 2
+
+
+def test_prefill_argument_checks():
+    lib = pkv.load_library()
+
+    def call(pool, **kw):
+        a = dict(q=A, q_dtype=pkv.PKV_BF16, qt=72 * 128, qh=128, b=1, s_q=1568, hq=8, table=A, ts=256, n_ctx=A,
+                 seq=A, cbs=0, maxk=6680, out=A, od=pkv.PKV_BF16)
+        a.update(kw)
+        return lib.pkv_attn_prefill_block_causal(ctypes.byref(pool), a["q"], a["q_dtype"], a["qt"], a["qh"], a["b"],
+                                                 a["s_q"], a["hq"], a["table"], a["ts"], a["n_ctx"], a["seq"],
+                                                 a["cbs"], a["maxk"], 0.1, a["out"], a["od"], None, None, 0, None)
+    p = _pool()
+    assert call(p, seq=None) == 1
+    assert call(p, cbs=-1) == 2
+    assert call(p, hq=12) == 2
+    assert call(p, maxk=256 * 32 + 1) == 2
+    assert call(p, q_dtype=pkv.PKV_F32) == 4
+    assert call(_pool(dtype=pkv.PKV_F32)) == 4
+    assert call(p, qt=72 * 128 + 1) == 6
+    assert call(p, s_q=0) == 0
+
+
+def test_merge_argument_checks():
+    lib = pkv.load_library()
+    assert lib.pkv_merge_states(None, A, 2, 10, 4, 128, A, 0, None, None) == 1
+    assert lib.pkv_merge_states(None, None, 2, 0, 4, 128, None, 0, None, None) == 0
+    assert lib.pkv_merge_states(A, A, 0, 10, 4, 128, A, 0, None, None) == 2
+    assert lib.pkv_merge_states(A, A, 2, 10, 4, 126, A, 0, None, None) == 2
+    assert lib.pkv_merge_states(A, A, 2, 10, 4, 128, A, 9, None, None) == 3
+    assert lib.pkv_merge_states(A, A, 2, 0, 4, 128, A, 0, None, None) == 0
+
+
+def test_workspace_sizes():
+    lib = pkv.load_library()
+    # 64 rows x 32 heads x 8 splits (4096 keys / 512) x (128 + 1) floats
+    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 4096) == 8 * 64 * 32 * 129 * 4
+    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 512) == 0      # one split
+    assert lib.pkv_attn_decode_workspace_bytes(256, 1, 64, 8, 128, 32768) == 16 * 256 * 64 * 129 * 4

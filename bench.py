@@ -1,0 +1,352 @@
+"""Benchmark of the paged K/V-cache path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 2,3,4,5] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The headline workload is the bf16 GQA decode (64
+sequences, lengths uniform in [512, 4096], 32 q / 8 kv heads of 128, 32-token
+pages in a 16384-page pool): one step = slot scatter of the step's 64 new
+tokens + paged decode, inputs resident in HBM.  ``value`` is the step's
+algorithmic bytes (K/V of every valid token once per kv head, Q, O, the table
+entries and lengths read, the scattered rows) over the measured step time.
+
+The other workloads (block-causal prefill, shared-prefix n-sample decode,
+long fp8 decode) are measured in the same run and reported under
+``"workloads"``; each timed step there is bracketed by HIP events on the
+launch stream with a 512 MiB write between steps (outside the events) so
+their working sets cannot stay in the 256 MiB Infinity Cache.
+
+``roofline`` describes the dominant call of the headline (the decode), timed
+with HIP events around each call inside the timed region; ``cpu_baseline``
+times the float64 CPU oracle (single thread) on a bounded sample of the same
+headline batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", default="3,4,5", help="secondary workloads to run (comma list of 3,4,5 or none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def to_dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def decode_bytes(kv_lens, page_size, hkv, d, kv_esize, n_rows_q, hq, q_esize, out_esize, with_lse, fp8_scales):
+    """Algorithmic bytes of one decode call: every valid K/V element once per kv
+    head, the used fp8 scales, Q, O, LSE, the table entries and lengths."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    pages = np.ceil(kv_lens / page_size).astype(np.int64)
+    b = 2 * int(kv_lens.sum()) * hkv * d * kv_esize
+    if fp8_scales:
+        b += 2 * int(pages.sum()) * hkv * 4
+    b += n_rows_q * hq * d * (q_esize + out_esize)
+    if with_lse:
+        b += n_rows_q * hq * 4
+    b += int(pages.sum()) * 4 + len(kv_lens) * 4
+    return b
+
+
+class Flusher:
+    """Writes 512 MiB between steps so the next step starts from HBM."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+
+    def __call__(self):
+        self.buf.fill_(1)
+
+
+def time_events(torch, step, reps, flush=None):
+    """Median/p10/p90 of per-step times (ms) from HIP events on the current stream."""
+    times = []
+    for _ in range(reps):
+        if flush:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    t = np.array(times)
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+# ----------------------------------------------------------------------------- headline: config 2
+
+def setup_decode_case(case, torch, pkv):
+    pool = pkv.Pool(to_dev(case.pool.k, torch), to_dev(case.pool.v, torch),
+                    None if case.pool.k_scale is None else to_dev(case.pool.k_scale, torch),
+                    None if case.pool.v_scale is None else to_dev(case.pool.v_scale, torch))
+    t, n, hq, d = case.q.shape
+    dev = dict(
+        pool=pool, q=to_dev(case.q, torch), tables=to_dev(case.tables, torch), lens=to_dev(case.kv_lens, torch),
+        out=torch.empty((t, n, hq, d), dtype=torch.bfloat16, device="cuda:0"),
+        ws=torch.empty(max(16, pkv.pkv_attn_decode_workspace_bytes(t, n, hq, case.pool.num_kv_heads, d,
+                                                                    case.max_kv_len)),
+                       dtype=torch.uint8, device="cuda:0"))
+    if case.slots is not None:
+        dev.update(new_k=to_dev(case.new_k, torch), new_v=to_dev(case.new_v, torch), slots=to_dev(case.slots, torch))
+    return dev
+
+
+def run_headline(args, torch, pkv, W):
+    case = W.config2()
+    dev = setup_decode_case(case, torch, pkv)
+    hkv, d = case.pool.num_kv_heads, case.pool.head_dim
+    t, n, hq, _ = case.q.shape
+    dec_bytes = decode_bytes(case.kv_lens, case.pool.page_size, hkv, d, 2, t * n, hq, 2, 2, False, False)
+    scat_bytes = 2 * 2 * len(case.slots) * hkv * d * 2 + len(case.slots) * 8
+    step_bytes = dec_bytes + scat_bytes
+    ev = []
+
+    def step(record=False):
+        pkv.pkv_scatter_slots(dev["pool"], dev["new_k"], dev["new_v"], dev["slots"])
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], case.max_kv_len, case.sm_scale,
+                            dev["out"], None, dev["ws"])
+        if record:
+            b.record()
+            ev.append((a, b))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flushed = time_events(torch, lambda: step(), 20, Flusher(torch))
+    return case, dict(step_bytes=step_bytes, dec_bytes=dec_bytes, ms_per_step=wall * 1e3, decode_ms=dec_ms,
+                      flushed_step_ms=flushed)
+
+
+# ----------------------------------------------------------------------------- secondary workloads
+
+def run_config3(torch, pkv, W, flush):
+    case = W.config3()
+    pool = pkv.Pool(to_dev(case.pool.k, torch), to_dev(case.pool.v, torch))
+    qkv = to_dev(case.qkv, torch)                       # [1, S, Hq + 2 Hkv, D]
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, qkv.shape[-1]
+    s_q = case.s_q
+    flat = qkv.view(s_q, hq + 2 * hkv, d)
+    k_src, v_src = flat[:, hq:hq + hkv], flat[:, hq + hkv:]
+    slots = to_dev(case.slots, torch)
+    tables, n_ctx, seq = to_dev(case.tables, torch), to_dev(case.n_ctx, torch), to_dev(case.seq_len, torch)
+    out = torch.empty((1, s_q, hq, d), dtype=torch.bfloat16, device="cuda:0")
+    q = qkv[:, :, :hq]
+
+    def scatter():
+        pkv.pkv_scatter_slots(pool, k_src, v_src, slots)
+
+    def prefill():
+        pkv.pkv_attn_prefill_block_causal(pool, q, tables, n_ctx, seq, case.causal_block_size, case.max_keys,
+                                          case.sm_scale, out)
+
+    try:
+        scatter()
+        prefill()
+        torch.cuda.synchronize()
+    except pkv.PkvError as e:
+        return {"error": str(e)}
+    for _ in range(5):
+        prefill()
+    seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
+    cbs = case.causal_block_size or seq_len
+    vis = sum(ctx + min((i // cbs + 1) * cbs, seq_len) for i in range(seq_len))
+    flops = 4.0 * d * hq * vis
+    med, p10, p90 = time_events(torch, prefill, 30, flush)
+    smed, _, _ = time_events(torch, scatter, 30, flush)
+    both, _, _ = time_events(torch, lambda: (scatter(), prefill()), 30, flush)
+    tflops = flops / (med * 1e-3) / 1e12
+    scat_bytes = 2 * 2 * seq_len * hkv * d * 2 + seq_len * 8
+    return {"workload": "bf16 block-causal prefill: 24 heads x 128, 1560 real queries (1568 rows) over a 1024 "
+                        "prefix + 4096 history + own block, 32-token pages",
+            "gflop": flops / 1e9, "prefill_ms": med, "prefill_ms_p10_p90": [p10, p90], "tflops": tflops,
+            "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "scatter_ms": smed,
+            "scatter_gbs": scat_bytes / (smed * 1e-3) / 1e9, "scatter_plus_prefill_ms": both}
+
+
+def run_config4(torch, pkv, W, flush):
+    c = W.config4()
+    pool = pkv.Pool(to_dev(c.pool.k, torch), to_dev(c.pool.v, torch))
+    new_k, new_v, slots = to_dev(c.new_k, torch), to_dev(c.new_v, torch), to_dev(c.slots, torch)
+    n_rows, hq, d, hkv = c.q.shape[0], c.num_q_heads, c.pool.head_dim, c.pool.num_kv_heads
+    g, s = c.num_groups, c.samples
+    q = to_dev(c.q, torch)
+    po = torch.empty((2, n_rows, hq, d), dtype=torch.float32, device="cuda:0")
+    pl = torch.empty((2, n_rows, hq), dtype=torch.float32, device="cuda:0")
+    out = torch.empty((n_rows, hq, d), dtype=torch.bfloat16, device="cuda:0")
+    mp, mt = int(c.prefix_lens.max()), int(c.tail_lens.max())
+    ws = torch.empty(max(16, pkv.pkv_attn_decode_workspace_bytes(g, s, hq, hkv, d, mp),
+                         pkv.pkv_attn_decode_workspace_bytes(n_rows, 1, hq, hkv, d, mt)),
+                     dtype=torch.uint8, device="cuda:0")
+    pt, plen = to_dev(c.prefix_tables, torch), to_dev(c.prefix_lens, torch)
+    tt, tlen = to_dev(c.tail_tables, torch), to_dev(c.tail_lens, torch)
+    ft, flen = to_dev(c.full_tables, torch), to_dev(c.full_lens, torch)
+    uout = torch.empty((n_rows, 1, hq, d), dtype=torch.bfloat16, device="cuda:0")
+    mf = int(c.full_lens.max())
+    ws2 = torch.empty(max(16, pkv.pkv_attn_decode_workspace_bytes(n_rows, 1, hq, hkv, d, mf)), dtype=torch.uint8,
+                      device="cuda:0")
+
+    def shared():
+        pkv.pkv_scatter_slots(pool, new_k, new_v, slots)
+        pkv.pkv_attn_decode(pool, q.view(g, s, hq, d), pt, plen, mp, c.sm_scale, po[0].view(g, s, hq, d),
+                            pl[0].view(g, s, hq), ws)
+        pkv.pkv_attn_decode(pool, q, tt, tlen, mt, c.sm_scale, po[1].view(n_rows, 1, hq, d),
+                            pl[1].view(n_rows, 1, hq), ws)
+        pkv.pkv_merge_states(po, pl, out)
+
+    def unshared():
+        pkv.pkv_scatter_slots(pool, new_k, new_v, slots)
+        pkv.pkv_attn_decode(pool, q, ft, flen, mf, c.sm_scale, uout, None, ws2)
+
+    for _ in range(5):
+        shared()
+        unshared()
+    med, p10, p90 = time_events(torch, shared, 30, flush)
+    umed, _, _ = time_events(torch, unshared, 30, flush)
+    pre = decode_bytes(c.prefix_lens, 32, hkv, d, 2, n_rows, hq, 2, 4, True, False)
+    tail = decode_bytes(c.tail_lens, 32, hkv, d, 2, n_rows, hq, 2, 4, True, False)
+    merge = 2 * n_rows * hq * (d + 1) * 4 + n_rows * hq * d * 2
+    scat = 2 * 2 * n_rows * hkv * d * 2 + n_rows * 8
+    total = pre + tail + merge + scat
+    gbs = total / (med * 1e-3) / 1e9
+    return {"workload": "shared-prefix n-sample decode: 8 prompts x 16 samples, 2048-token shared prefix, tails "
+                        "U[1,512], 32/8 heads x 128, bf16 (scatter + prefix decode + tail decode + merge)",
+            "algorithmic_mb": total / 1e6, "step_ms": med, "step_ms_p10_p90": [p10, p90], "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "unshared_step_ms": umed,
+            "unshared_mb": (decode_bytes(c.full_lens, 32, hkv, d, 2, n_rows, hq, 2, 2, False, False) + scat) / 1e6}
+
+
+def run_config5(torch, pkv, W, flush):
+    c = W.config5()
+    dev = setup_decode_case(c, torch, pkv)
+    t, n, hq, d = c.q.shape
+    hkv = c.pool.num_kv_heads
+
+    def step():
+        pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], c.max_kv_len, c.sm_scale,
+                            dev["out"], None, dev["ws"])
+
+    for _ in range(3):
+        step()
+    med, p10, p90 = time_events(torch, step, 20, flush)
+    nbytes = decode_bytes(c.kv_lens, 32, hkv, d, 1, t * n, hq, 2, 2, False, True)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return {"workload": "fp8 decode: 256 sequences, lengths log-uniform in [1024, 32768], 64/8 heads x 128, "
+                        "e4m3fn K/V with per-(page, kv head) scales, bf16 q/out",
+            "algorithmic_gb": nbytes / 1e9, "decode_ms": med, "decode_ms_p10_p90": [p10, p90], "gbs": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(case, seconds):
+    """Time the float64 oracle (one BLAS thread) on the headline batch's first
+    tables until about ``seconds`` of CPU work; report the same algorithmic
+    bytes per second as the GPU figure."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as orc
+
+    kp = orc.scatter_slots(case.pool.k, case.new_k, case.slots)
+    vp = orc.scatter_slots(case.pool.v, case.new_v, case.slots)
+    hkv, d = case.pool.num_kv_heads, case.pool.head_dim
+    done, spent = [], 0.0
+    with threadpool_limits(limits=1):
+        for t in range(len(case.kv_lens)):
+            t0 = time.perf_counter()
+            orc.attn_decode(kp, vp, case.q, case.tables, case.kv_lens, case.sm_scale, tables_subset=[t])
+            spent += time.perf_counter() - t0
+            done.append(t)
+            if spent >= seconds:
+                break
+    lens = case.kv_lens[done]
+    nbytes = decode_bytes(lens, case.pool.page_size, hkv, d, 2, len(done), case.num_q_heads, 2, 2, False, False)
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle decode of {len(done)} of the 64 sequences ({int(lens.sum())} keys, "
+                      f"{nbytes / 1e6:.1f} MB algorithmic) after its own scatter; {spent:.1f} s on one thread"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_slots_amd as pkv
+    import workloads as W
+
+    pkv.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    case, h = run_headline(args, torch, pkv, W)
+    value = h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9
+    achieved = h["dec_bytes"] / (h["decode_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": "paged decode K/V GB/s (% HBM peak) + block-causal prefill TFLOP/s (% MFMA)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "bf16 GQA paged decode: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads x 128, "
+                               "32-token pages shuffled over a 16384-page pool; step = scatter of 64 new tokens + "
+                               "decode",
+                   "global_batch": 64, "seq_len": int(case.max_kv_len), "total_keys": int(case.kv_lens.sum()),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pkv_attn_decode call (decode kernel + split merge kernel)",
+                     "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
+        "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],
+    }
+    workloads = {}
+    flush = Flusher(torch)
+    for cfg in [c for c in args.configs.split(",") if c.strip() and c != "none"]:
+        fn = {"3": run_config3, "4": run_config4, "5": run_config5}[cfg.strip()]
+        workloads[f"config{cfg.strip()}"] = fn(torch, pkv, W, flush)
+        torch.cuda.empty_cache()
+    if workloads:
+        result["workloads"] = workloads
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -88,56 +88,56 @@ struct TileRegs {
   static constexpr int KLD = kFp8 ? NCH / 2 : NCH;    // 16-byte K loads per half
   static constexpr int VB = kFp8 ? D / 16 : D / 8;    // bytes per V block row (D/16 dims)
   u32x4 k[2][KLD];
-  // V: 8 keys x (D/16) dims; stored as dwords
-  uint32_t v[8][VB / 4 > 0 ? VB / 4 : 1];
-  int32_t page0, page1;
+  uint32_t v[8][VB / 4 > 0 ? VB / 4 : 1];             // 8 keys x (D/16) dims, as dwords
   float ks0, ks1, vs0, vs1;
 };
 
+// Byte offsets of this lane inside a page that stay fixed along the key walk.
+struct LaneOffsets {
+  int k;   // K: key row (lane & 15) of a 16-key half, dims chunk of lane group
+  int v;   // V: key row 4 * (lane >> 4) of a half, dims (D/16) * (lane & 15)
+};
+
+// A raw buffer descriptor over one page's rows of one kv head.  With
+// nbytes = 0 every load through it returns zeros without touching memory,
+// which is how a prefetch past the end of the key range is made harmless.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pool, int page, int64_t page_stride_b,
+                                                            int64_t head_off_b, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pool + (int64_t)page * page_stride_b + head_off_b),
+                                           (short)0, nbytes, 0x00020000);
+}
+
+// Issue the loads of one tile (two 16-key halves at rows row0 / row1 of
+// pages page0 / page1).  Addresses are SGPR descriptors + per-lane constant
+// offsets, so the walk costs no vector address arithmetic.
 template <int D, bool kFp8>
-__device__ __forceinline__ void load_tile(TileRegs<D, kFp8>& r, const DecodeParams& p, int g, int page0,
-                                          int page1, int key0) {
+__device__ __forceinline__ void issue_tile(TileRegs<D, kFp8>& r, const uint8_t* kp, const uint8_t* vp, int page0,
+                                           int page1, int row0, int row1, int64_t page_stride_b, int64_t head_off_b,
+                                           int row_b, int nbytes, LaneOffsets lo) {
   using T = TileRegs<D, kFp8>;
-  const int lane = threadIdx.x & 63;
-  const int kk = lane & 15, j = lane >> 4;
-  constexpr int esz = kFp8 ? 1 : 2;
-  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
-  const int mask = (1 << p.page_shift) - 1;
-  const int row0 = key0 & mask;
-  const int row1 = (key0 + 16) & mask;
-  const int64_t base0 = (int64_t)page0 * p.page_stride + (int64_t)g * D;
-  const int64_t base1 = (int64_t)page1 * p.page_stride + (int64_t)g * D;
-  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k_pool);
-  const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v_pool);
-  // K: lane = key kk of each half; chunk dims per lane group j
+  const __amdgpu_buffer_rsrc_t k0 = page_rsrc(kp, page0, page_stride_b, head_off_b, nbytes);
+  const __amdgpu_buffer_rsrc_t k1 = page_rsrc(kp, page1, page_stride_b, head_off_b, nbytes);
+  const __amdgpu_buffer_rsrc_t v0 = page_rsrc(vp, page0, page_stride_b, head_off_b, nbytes);
+  const __amdgpu_buffer_rsrc_t v1 = page_rsrc(vp, page1, page_stride_b, head_off_b, nbytes);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t kb = (h == 0 ? base0 + (row0 + kk) * row_elems : base1 + (row1 + kk) * row_elems);
-#pragma unroll
-    for (int c = 0; c < T::KLD; ++c) {
-      const int dim = kFp8 ? (64 * c + 16 * j) : (32 * c + 8 * j);
-      r.k[h][c] = ld16(kp + (kb + dim) * esz);
-    }
+  for (int c = 0; c < T::KLD; ++c) {
+    r.k[0][c] = __builtin_amdgcn_raw_buffer_load_b128(k0, lo.k + 64 * c, row0 * row_b, 0);
+    r.k[1][c] = __builtin_amdgcn_raw_buffer_load_b128(k1, lo.k + 64 * c, row1 * row_b, 0);
   }
-  // V: keys 4j..4j+3 of half 0 and of half 1, dims (D/16)*kk ..
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const int h = t >> 2;
-    const int row = (h == 0 ? row0 : row1) + 4 * j + (t & 3);
-    const int64_t vb = (h == 0 ? base0 : base1) + row * row_elems + (D / 16) * kk;
-    const uint8_t* src = vp + vb * esz;
+    const __amdgpu_buffer_rsrc_t rs = (t < 4) ? v0 : v1;
+    const int soff = ((t < 4 ? row0 : row1) + (t & 3)) * row_b;
     if constexpr (T::VB == 16) {
-      const u32x4 x = ld16(src);
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v, soff, 0);
       r.v[t][0] = x[0]; r.v[t][1] = x[1]; r.v[t][2] = x[2]; r.v[t][3] = x[3];
     } else if constexpr (T::VB == 8) {
-      const u32x2 x = ld8(src);
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, lo.v, soff, 0);
       r.v[t][0] = x[0]; r.v[t][1] = x[1];
     } else {
-      r.v[t][0] = *reinterpret_cast<const uint32_t*>(src);
+      r.v[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lo.v, soff, 0);
     }
   }
-  r.page0 = page0;
-  r.page1 = page1;
 }
 
 // Running softmax state of one wave (16 rows, lane row = lane & 15).
@@ -278,19 +278,124 @@ __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>&
   }
 }
 
+// Q operand chunks of this lane's query row (zeros for a padding row).  The
+// dims of chunk i / lane group j match the K operand layout of the tile.
+template <int D, bool kFp8>
+__device__ __forceinline__ void load_q(u32x4 (&q)[D / 32], const DecodeParams& p, int64_t qrow, bool row_ok) {
+  const int j = (threadIdx.x & 63) >> 4;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow * D;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int dim = kFp8 ? (64 * (i >> 1) + 16 * j + 8 * (i & 1)) : (32 * i + 8 * j);
+    q[i] = row_ok ? ld16(qp + dim) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void reset_state(RowState<D>& st) {
+#pragma unroll
+  for (int tp = 0; tp < D / 16; ++tp) st.o[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
+}
+
+// Walk the tiles first, first + step, ... (n of them) of one (table row, kv
+// head): windows of 64 tiles get their page ids (and fp8 scales) with one
+// vector load; inside a window every tile is prefetched one step ahead with
+// unconditional loads (zero-range descriptor past the window's end).
+template <int D, bool kFp8>
+__device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
+                                           const int32_t* trow, int g, int len, int first, int step, int n) {
+  constexpr int esz = kFp8 ? 1 : 2;
+  const int lane = threadIdx.x & 63;
+  const int r_lane = lane & 15, j = lane >> 4;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v_pool);
+  const int64_t page_stride_b = p.page_stride * esz;
+  const int64_t head_off_b = (int64_t)g * D * esz;
+  const int row_b = p.num_kv_heads * D * esz;
+  const int page_bytes = (1 << p.page_shift) * row_b;
+  const int pmask = (1 << p.page_shift) - 1;
+  const LaneOffsets lo{r_lane * row_b + 16 * j, 4 * j * row_b + (D / 16) * r_lane * esz};
+  const int te = first + (n - 1) * step + 1;   // one past the last tile walked
+  TileRegs<D, kFp8> A, B;
+  for (int w0 = 0; w0 < n; w0 += 64) {
+    const PageWindow win = fetch_pages<kFp8>(p, trow, g, first + w0 * step, step, te, len);
+    const int n_win = n - w0 < 64 ? n - w0 : 64;
+    auto issue = [&](TileRegs<D, kFp8>& X, int k) {
+      const bool ok = k < n_win;
+      const int kc = ok ? k : 0;
+      const int key0 = (first + (w0 + kc) * step) * 32;
+      issue_tile<D, kFp8>(X, kp, vp, rl(win.e0, kc), rl(win.e1, kc), key0 & pmask, (key0 + 16) & pmask,
+                          page_stride_b, head_off_b, row_b, ok ? page_bytes : 0, lo);
+      if constexpr (kFp8) {
+        X.ks0 = rlf(win.ks0, kc);
+        X.ks1 = rlf(win.ks1, kc);
+        X.vs0 = rlf(win.vs0, kc);
+        X.vs1 = rlf(win.vs1, kc);
+      }
+    };
+    issue(A, 0);
+    for (int k = 0; k < n_win; k += 2) {
+      issue(B, k + 1);
+      compute_tile<D, kFp8>(st, A, q, p.scale_log2, (first + (w0 + k) * step) * 32, len);
+      if (k + 1 >= n_win) break;
+      issue(A, k + 2);
+      compute_tile<D, kFp8>(st, B, q, p.scale_log2, (first + (w0 + k + 1) * step) * 32, len);
+    }
+  }
+}
+
+// Store the normalised rows of a finished state: lane (r, j) holds dims
+// DPL*(4j+i) + t' of row r.  `dst` points at the row's D outputs.
+template <int D>
+__device__ __forceinline__ void store_row(const RowState<D>& st, void* dst, bool bf16, float inv) {
+  constexpr int DPL = D / 16;
+  const int j = (threadIdx.x & 63) >> 4;
+  if (bf16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w[DPL / 2];
+#pragma unroll
+      for (int tp = 0; tp < DPL; tp += 2) w[tp / 2] = pack_bf16x2(st.o[tp][i] * inv, st.o[tp + 1][i] * inv);
+      uint16_t* d = o + DPL * (4 * j + i);
+      if constexpr (DPL == 8) *reinterpret_cast<u32x4*>(d) = u32x4{w[0], w[1], w[2], w[3]};
+      else *reinterpret_cast<u32x2*>(d) = u32x2{w[0], w[1]};
+    }
+  } else {
+    float* o = reinterpret_cast<float*>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tp = 0; tp < DPL; tp += 4)
+        *reinterpret_cast<f32x4*>(o + DPL * (4 * j + i) + tp) =
+            f32x4{st.o[tp][i] * inv, st.o[tp + 1][i] * inv, st.o[tp + 2][i] * inv, st.o[tp + 3][i] * inv};
+  }
+}
+
+__device__ __forceinline__ void row_of(const DecodeParams& p, int t, int g, int r, int& qi, int64_t& qrow) {
+  qi = r / p.group;
+  const int qh = g * p.group + (r - qi * p.group);
+  qrow = ((int64_t)t * p.rows_per_table + qi) * p.num_q_heads + qh;
+}
+
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Split kernel: one workgroup per (key split, kv head, table row, row group).
+// Used without a stream-K workspace; with splits == 1 it needs no workspace.
+// ---------------------------------------------------------------------------
 template <int D, bool kFp8, int WP>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   constexpr int WR = 4 / WP;
-  constexpr int NCH = D / 32;
   constexpr int DPL = D / 16;
   const int s = blockIdx.x;
   const int g = blockIdx.y;
   const int n_rg = gridDim.z / p.num_tables;
   const int t = blockIdx.z / n_rg;
   const int rg = blockIdx.z - t * n_rg;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wr = wave / WP, wp = wave - (wave / WP) * WP;
   const int lane = threadIdx.x & 63;
   const int r_lane = lane & 15, j = lane >> 4;
@@ -304,63 +409,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   te = te < tiles ? te : tiles;
   if (p.splits > 1 && tb >= te) return;   // empty split: the merge never reads it
 
-  // ---- this lane's query row and its Q operand chunks
   const int r = rb * 16 + r_lane;
   const bool row_ok = r < R;
-  const int qi = row_ok ? r / p.group : 0;
-  const int qh = g * p.group + (row_ok ? r - qi * p.group : 0);
-  const int64_t qrow = ((int64_t)t * p.rows_per_table + qi) * p.num_q_heads + qh;
-  u32x4 q[NCH];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qrow * D;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int dim = kFp8 ? (64 * (i >> 1) + 16 * j + 8 * (i & 1)) : (32 * i + 8 * j);
-      q[i] = row_ok ? ld16(qp + dim) : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
+  int qi;
+  int64_t qrow;
+  row_of(p, t, g, row_ok ? r : 0, qi, qrow);
+  u32x4 q[D / 32];
+  load_q<D, kFp8>(q, p, qrow, row_ok);
   RowState<D> st;
-#pragma unroll
-  for (int tp = 0; tp < DPL; ++tp) st.o[tp] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = kNegInf;
-  st.l = 0.f;
-
-  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  reset_state(st);
   const int first = tb + wp;
   const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
-  if (rb * 16 < R && n_mine > 0) {
-    TileRegs<D, kFp8> A, B;
-    PageWindow win = fetch_pages<kFp8>(p, trow, g, first, WP, te, len);
-    // Load the registers of the wave's it-th tile; page ids come from the
-    // window, refreshed every 64 tiles.
-    auto prep = [&](TileRegs<D, kFp8>& X, int it) {
-      const int k = it & 63;
-      if (k == 0 && it > 0) win = fetch_pages<kFp8>(p, trow, g, first + it * WP, WP, te, len);
-      load_tile<D, kFp8>(X, p, g, rl(win.e0, k), rl(win.e1, k), (first + it * WP) * 32);
-      if constexpr (kFp8) {
-        X.ks0 = rlf(win.ks0, k);
-        X.ks1 = rlf(win.ks1, k);
-        X.vs0 = rlf(win.vs0, k);
-        X.vs1 = rlf(win.vs1, k);
-      }
-    };
-    // two register sets: the next tile is in flight while this one computes
-    prep(A, 0);
-    for (int it = 0; it < n_mine; it += 2) {
-      if (it + 1 < n_mine) prep(B, it + 1);
-      compute_tile<D, kFp8>(st, A, q, p.scale_log2, (first + it * WP) * 32, len);
-      if (it + 1 >= n_mine) break;
-      if (it + 2 < n_mine) prep(A, it + 2);
-      compute_tile<D, kFp8>(st, B, q, p.scale_log2, (first + (it + 1) * WP) * 32, len);
-    }
-  }
+  if (rb * 16 < R && n_mine > 0)
+    walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, first, WP, n_mine);
 
-  // ---- full row sum of this wave
   st.l += __shfl_xor(st.l, 16, 64);
   st.l += __shfl_xor(st.l, 32, 64);
 
-  // ---- combine the WP tile-split waves of each row block through LDS
+  // combine the WP tile-split waves of each row block through LDS
   if constexpr (WP > 1) {
     __shared__ float sm_ml[4][2][16];
     __shared__ f32x4 sm_o[4][64][DPL];
@@ -394,43 +460,188 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   }
   if (!row_ok) return;
 
-  // ---- normalise and store: this lane holds dims DPL*(4j+i) + t' of its row
   const bool empty = st.l == 0.f;
   const float inv = empty ? 0.f : 1.0f / st.l;
   const float lse = empty ? kNegInf : (st.m + fast_log2(st.l)) * kLn2;
   if (p.splits == 1) {
-    if (p.out_bf16) {
-      uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + qrow * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t w[DPL / 2];
-#pragma unroll
-        for (int tp = 0; tp < DPL; tp += 2) w[tp / 2] = pack_bf16x2(st.o[tp][i] * inv, st.o[tp + 1][i] * inv);
-        uint16_t* dst = o + DPL * (4 * j + i);
-        if constexpr (DPL == 8) *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-        else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-      }
-    } else {
-      float* o = reinterpret_cast<float*>(p.out) + qrow * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tp = 0; tp < DPL; tp += 4)
-          *reinterpret_cast<f32x4*>(o + DPL * (4 * j + i) + tp) =
-              f32x4{st.o[tp][i] * inv, st.o[tp + 1][i] * inv, st.o[tp + 2][i] * inv, st.o[tp + 3][i] * inv};
-    }
+    store_row<D>(st, reinterpret_cast<uint8_t*>(p.out) + qrow * D * (p.out_bf16 ? 2 : 4), p.out_bf16, inv);
     if (p.out_lse && j == 0) p.out_lse[qrow] = lse;
   } else {
     const int64_t plane = (int64_t)p.num_tables * p.rows_per_table * p.num_q_heads;
-    float* o = p.ws_o + ((int64_t)s * plane + qrow) * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int tp = 0; tp < DPL; tp += 4)
-        *reinterpret_cast<f32x4*>(o + DPL * (4 * j + i) + tp) =
-            f32x4{st.o[tp][i] * inv, st.o[tp + 1][i] * inv, st.o[tp + 2][i] * inv, st.o[tp + 3][i] * inv};
+    store_row<D>(st, p.ws_o + ((int64_t)s * plane + qrow) * D, false, inv);
     if (j == 0) p.ws_lse[(int64_t)s * plane + qrow] = lse;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K kernel: a persistent grid of workers (WR waves each: the row
+// blocks of one (table row, kv head, row group) unit).  The flattened list of
+// (unit, tile) positions is cut into equal contiguous chunks, one per worker,
+// so every worker streams the same number of tiles whatever the length mix.
+// A worker walks its chunk across unit boundaries: a unit it covers whole is
+// stored as final output; a unit cut by a chunk boundary leaves a normalised
+// partial state (output + LSE) in slot 2w (the worker's first segment) or
+// 2w+1 (its last), joined afterwards by merge_sk_kernel.  The cut points
+// depend only on the lengths, never on page ids, so results are independent
+// of where pages sit in the pool.
+// ---------------------------------------------------------------------------
+template <int D, bool kFp8, int WR>
+__global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
+  constexpr int WPW = 4 / WR;   // workers per workgroup
+  __shared__ int32_t cum[kMaxSkTables + 1];
+  __shared__ int32_t part[256];
+  const int T = p.num_tables;
+  // ---- prefix sums of tiles per table row (every workgroup, from kv_lens)
+  {
+    const int per = (T + 255) / 256;
+    const int lo = threadIdx.x * per;
+    int run = 0;
+    for (int i = 0; i < per && lo + i < T; ++i) run += (p.kv_lens[lo + i] + 31) >> 5;
+    part[threadIdx.x] = run;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int acc = part[threadIdx.x] - run;   // exclusive prefix of this thread's run
+    for (int i = 0; i < per && lo + i < T; ++i) {
+      cum[lo + i] = acc;
+      acc += (p.kv_lens[lo + i] + 31) >> 5;
+    }
+    if (threadIdx.x == 255) cum[T] = part[255];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i <= T; i += 256) p.ws_cum[i] = cum[i];
+  }
+  const int R = p.rows_per_table * p.group;
+  const int HR = p.num_kv_heads * p.row_groups;   // units per table row
+  const int64_t N = (int64_t)cum[T] * HR;
+  const int64_t C = (N + p.n_workers - 1) / p.n_workers;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x * WPW + wave / WR;
+  const int wr = wave - (wave / WR) * WR;
+  const int lane = threadIdx.x & 63;
+  const int r_lane = lane & 15, j = lane >> 4;
+  const int64_t c_begin = (int64_t)worker * C;
+  const int64_t c_end = c_begin + C < N ? c_begin + C : N;
+  if (c_begin >= c_end) return;
+  // the table row holding flattened position c_begin: largest t with cum[t]*HR <= c_begin
+  int t = 0;
+  {
+    int lo = 0, hi = T;   // invariant: cum[lo]*HR <= c_begin < cum[hi]*HR
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)cum[mid] * HR <= c_begin) lo = mid; else hi = mid;
+    }
+    t = lo;
+  }
+  int64_t c = c_begin;
+  while (c < c_end) {
+    const int tiles = cum[t + 1] - cum[t];
+    if (tiles == 0) { ++t; continue; }
+    const int64_t off = c - (int64_t)cum[t] * HR;
+    const int ui = (int)(off / tiles);
+    const int k0 = (int)(off - (int64_t)ui * tiles);
+    const int k1 = (int64_t)tiles < k0 + (c_end - c) ? tiles : (int)(k0 + (c_end - c));
+    const int g = ui / p.row_groups;
+    const int rg = ui - g * p.row_groups;
+    const int rb = rg * WR + wr;
+    const int r = rb * 16 + r_lane;
+    const bool row_ok = r < R;
+    int qi;
+    int64_t qrow;
+    row_of(p, t, g, row_ok ? r : 0, qi, qrow);
+    u32x4 q[D / 32];
+    load_q<D, kFp8>(q, p, qrow, row_ok);
+    RowState<D> st;
+    reset_state(st);
+    const int len = p.kv_lens[t];
+    if (rb * 16 < R)
+      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, k0, 1, k1 - k0);
+    st.l += __shfl_xor(st.l, 16, 64);
+    st.l += __shfl_xor(st.l, 32, 64);
+    const bool empty = st.l == 0.f;
+    const float inv = empty ? 0.f : 1.0f / st.l;
+    const float lse = empty ? kNegInf : (st.m + fast_log2(st.l)) * kLn2;
+    if (row_ok) {
+      if (k0 == 0 && k1 == tiles) {
+        store_row<D>(st, reinterpret_cast<uint8_t*>(p.out) + qrow * D * (p.out_bf16 ? 2 : 4), p.out_bf16, inv);
+        if (p.out_lse && j == 0) p.out_lse[qrow] = lse;
+      } else {
+        const int slot = 2 * worker + (c == c_begin ? 0 : 1);
+        const int64_t prow = (int64_t)slot * (16 * WR) + wr * 16 + r_lane;
+        store_row<D>(st, p.ws_o + prow * D, false, inv);
+        if (j == 0) p.ws_lse[prow] = lse;
+      }
+    }
+    c += k1 - k0;
+    if (ui + 1 == HR) ++t;
+  }
+}
+
+// Joins the partial states of units cut by chunk boundaries, and writes the
+// zero output / -inf LSE of table rows with no keys.  One thread per (row,
+// 4 dims) of every unit; units a single worker finished are skipped.
+__global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_per_worker, int head_dim) {
+  const int D = head_dim;
+  const int chunks = D >> 2;
+  const int R = p.rows_per_table * p.group;
+  const int64_t total = (int64_t)p.num_tables * p.num_kv_heads * R * chunks;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int ch = (int)(tid % chunks);
+  const int64_t rest = tid / chunks;
+  const int r = (int)(rest % R);
+  const int64_t tg = rest / R;
+  const int g = (int)(tg % p.num_kv_heads);
+  const int t = (int)(tg / p.num_kv_heads);
+  const int rows_w = 16 * wr_per_worker;
+  const int rg = r / rows_w;
+  const int HR = p.num_kv_heads * p.row_groups;
+  const int T = p.num_tables;
+  const int64_t N = (int64_t)p.ws_cum[T] * HR;
+  const int64_t C = (N + p.n_workers - 1) / p.n_workers;
+  const int tiles = p.ws_cum[t + 1] - p.ws_cum[t];
+  int qi;
+  int64_t qrow;
+  row_of(p, t, g, r, qi, qrow);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse_out = kNegInf;
+  if (tiles > 0) {
+    const int64_t F = (int64_t)p.ws_cum[t] * HR + (int64_t)(g * p.row_groups + rg) * tiles;
+    const int64_t w0 = F / C, w1 = (F + tiles - 1) / C;
+    if (w0 == w1) return;   // finished by one worker
+    const int row_in = r - rg * rows_w;
+    float m = kNegInf;
+    for (int64_t w = w0; w <= w1; ++w) {
+      const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
+      m = fmaxf(m, p.ws_lse[slot * rows_w + row_in]);
+    }
+    if (m != kNegInf) {
+      float wsum = 0.f;
+      for (int64_t w = w0; w <= w1; ++w) {
+        const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
+        const float lw = p.ws_lse[slot * rows_w + row_in];
+        const float f = fast_exp2((lw - m) * kLog2e);
+        if (f > 0.f) {
+          acc += f * *reinterpret_cast<const f32x4*>(p.ws_o + (slot * rows_w + row_in) * D + 4 * ch);
+          wsum += f;
+        }
+      }
+      acc *= 1.0f / wsum;
+      lse_out = m + fast_log2(wsum) * kLn2;
+    }
+  }
+  const int64_t o_off = qrow * D + 4 * ch;
+  if (p.out_bf16) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + o_off) =
+        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o_off) = acc;
+  }
+  if (p.out_lse && ch == 0) p.out_lse[qrow] = lse_out;
 }
 
 // ---------------------------------------------------------------------------
@@ -559,6 +770,50 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return kv == kFP8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
   return kv == kFP8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
+}
+
+int sk_waves_per_worker(int rows_per_unit) {
+  const int blocks16 = (rows_per_unit + 15) / 16;
+  return blocks16 <= 1 ? 1 : blocks16 <= 2 ? 2 : 4;
+}
+
+template <int D, bool kFp8, int WR>
+static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream) {
+  // a persistent grid: as many workgroups as stay resident at once
+  static int resident[2] = {0, 0};   // per-kernel occupancy, queried once
+  int& per_cu = resident[0];
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int blocks = per_cu * sm_count;
+  p.n_workers = blocks * (4 / WR);
+  if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
+  const int grid = p.n_workers / (4 / WR);
+  hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int R = p.rows_per_table * p.group;
+  const int64_t total = (int64_t)p.num_tables * p.num_kv_heads * R * (D / 4);
+  hipLaunchKernelGGL(merge_sk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p, WR, D);
+  return hipGetLastError();
+}
+
+template <int D, bool kFp8>
+static hipError_t launch_sk_d(const DecodeParams& p, int sm_count, hipStream_t stream) {
+  switch (sk_waves_per_worker(p.rows_per_table * p.group)) {
+    case 1: return launch_sk_dw<D, kFp8, 1>(p, sm_count, stream);
+    case 2: return launch_sk_dw<D, kFp8, 2>(p, sm_count, stream);
+    default: return launch_sk_dw<D, kFp8, 4>(p, sm_count, stream);
+  }
+}
+
+hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream) {
+  if (head_dim == 128) return kv == kFP8 ? launch_sk_d<128, true>(p, sm_count, stream) : launch_sk_d<128, false>(p, sm_count, stream);
+  return kv == kFP8 ? launch_sk_d<64, true>(p, sm_count, stream) : launch_sk_d<64, false>(p, sm_count, stream);
 }
 
 template <int D, int QT>

@@ -18,8 +18,14 @@ constexpr int kAbiVersion = 1;
 // splits ("Support shared-prefix attention for n-sample requests in FMHA",
 // split-KV and MIN_SPLIT_TOKENS commit messages).  The split count depends on
 // host arguments only, so the workspace size is known before the call.
-constexpr int kMinSplitTokens = 512;
-constexpr int kMaxSplits = 16;
+#ifndef PKV_MIN_SPLIT_TOKENS
+#define PKV_MIN_SPLIT_TOKENS 512
+#endif
+#ifndef PKV_MAX_SPLITS
+#define PKV_MAX_SPLITS 16
+#endif
+constexpr int kMinSplitTokens = PKV_MIN_SPLIT_TOKENS;
+constexpr int kMaxSplits = PKV_MAX_SPLITS;
 
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3FN; }
 int elem_bytes(pkv_dtype d) { return d == PKV_F32 ? 4 : d == PKV_BF16 ? 2 : 1; }
@@ -59,6 +65,28 @@ size_t decode_ws_bytes(int64_t rows, int32_t num_q_heads, int32_t head_dim, int 
   if (splits <= 1) return 0;
   const int64_t plane = rows * num_q_heads;
   return (size_t)(splits * plane * (int64_t)(head_dim + 1) * (int64_t)sizeof(float));
+}
+
+// Stream-K workspace: prefix sums of tiles per table row, then the partial
+// states (output rows, then their LSE) of every wave's two slots.
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+int64_t sk_cum_bytes(int32_t num_tables) { return align256(4 * (int64_t)(num_tables + 1)); }
+int64_t sk_rows() { return 2 * (int64_t)kMaxSkWaves * 16; }
+size_t sk_ws_bytes(int32_t num_tables, int32_t head_dim) {
+  return (size_t)(sk_cum_bytes(num_tables) + align256(sk_rows() * head_dim * 4) + align256(sk_rows() * 4));
+}
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -124,7 +152,9 @@ size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_tabl
   (void)num_kv_heads;
   if (num_tables <= 0 || rows_per_table <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   const SplitPlan plan = plan_decode(max_kv_len);
-  return decode_ws_bytes((int64_t)num_tables * rows_per_table, num_q_heads, head_dim, plan.splits);
+  const size_t split = decode_ws_bytes((int64_t)num_tables * rows_per_table, num_q_heads, head_dim, plan.splits);
+  const size_t sk = num_tables <= kMaxSkTables ? sk_ws_bytes(num_tables, head_dim) : 0;
+  return split > sk ? split : sk;
 }
 
 pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
@@ -157,9 +187,17 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   }
 
   const int64_t rows = (int64_t)num_tables * rows_per_table;
+  // Stream-K (balanced persistent grid) when the workspace holds its state.
+  const int R = rows_per_table * (num_q_heads / pool->num_kv_heads);
+  const int sk_wr = sk_waves_per_worker(R);
+  const int sk_rg = (int)ceil_div(ceil_div(R, 16), sk_wr);
+  const int64_t sk_positions = (int64_t)num_tables * ceil_div(max_kv_len, 32) * pool->num_kv_heads * sk_rg;
+  const int cus = use_mfma ? device_cu_count() : 0;
+  const bool use_sk = use_mfma && cus > 0 && workspace && aligned(workspace, 256) && num_tables <= kMaxSkTables &&
+                      workspace_bytes >= sk_ws_bytes(num_tables, D) && sk_positions < (int64_t(1) << 31);
   SplitPlan plan = plan_decode(max_kv_len);
   const size_t need = decode_ws_bytes(rows, num_q_heads, D, plan.splits);
-  if (plan.splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) {
+  if (use_sk || (plan.splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))) {
     plan.splits = 1;
     plan.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(max_kv_len, 32));
   }
@@ -176,7 +214,13 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   p.out_lse = out_lse;
   p.ws_o = nullptr;
   p.ws_lse = nullptr;
-  if (plan.splits > 1) {
+  p.ws_cum = nullptr;
+  if (use_sk) {
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    p.ws_cum = reinterpret_cast<int32_t*>(w);
+    p.ws_o = reinterpret_cast<float*>(w + sk_cum_bytes(num_tables));
+    p.ws_lse = reinterpret_cast<float*>(w + sk_cum_bytes(num_tables) + align256(sk_rows() * D * 4));
+  } else if (plan.splits > 1) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + (int64_t)plan.splits * rows * num_q_heads * D;
   }
@@ -191,8 +235,11 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   p.splits = plan.splits;
   p.tiles_per_split = plan.tiles_per_split;
   p.out_bf16 = out_dtype == PKV_BF16;
+  p.n_workers = 0;
+  p.row_groups = sk_rg;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
 
+  if (use_sk) return launch_decode_sk(p, elem_type(pool->dtype), D, cus, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
   hipError_t e = use_mfma ? launch_decode_mfma(p, elem_type(pool->dtype), D, stream)
                           : launch_decode_valu(p, elem_type(q_dtype), elem_type(pool->dtype), D, stream);
   if (e != hipSuccess) return PKV_ERR_HIP;

@@ -12,6 +12,11 @@ namespace pkv {
 
 enum ElemType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
+// Stream-K decode limits: table rows whose prefix sums fit LDS, and partial
+// state rows in the workspace (2 slots x 16 rows per wave of every worker).
+constexpr int kMaxSkTables = 8192;
+constexpr int kMaxSkWaves = 4096;
+
 struct ScatterParams {
   const uint8_t* src_k;
   const uint8_t* src_v;
@@ -43,6 +48,7 @@ struct DecodeParams {
   float* out_lse;             // nullable
   float* ws_o;                // [splits, T, n, Hq, D] when splits > 1
   float* ws_lse;              // [splits, T, n, Hq]
+  int32_t* ws_cum;            // stream-K: [T + 1] prefix sums of tiles per table row
   int64_t page_stride;        // elements
   int32_t page_shift;
   int32_t num_kv_heads;
@@ -54,6 +60,8 @@ struct DecodeParams {
   int32_t splits;             // cross-workgroup key splits
   int32_t tiles_per_split;    // 32-key tiles per split
   int32_t out_bf16;
+  int32_t n_workers;          // stream-K workers (set by the launcher)
+  int32_t row_groups;         // stream-K: row groups per (table row, kv head)
   float scale_log2;           // sm_scale * log2(e)
 };
 
@@ -100,6 +108,8 @@ struct PrefillParams {
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);
+int sk_waves_per_worker(int rows_per_unit);
+hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);

@@ -115,7 +115,11 @@ def test_merge_argument_checks():
 
 def test_workspace_sizes():
     lib = pkv.load_library()
-    # 64 rows x 32 heads x 8 splits (4096 keys / 512) x (128 + 1) floats
-    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 4096) == 8 * 64 * 32 * 129 * 4
-    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 512) == 0      # one split
-    assert lib.pkv_attn_decode_workspace_bytes(256, 1, 64, 8, 128, 32768) == 16 * 256 * 64 * 129 * 4
+    # the larger of: key splits (8 x 64 rows x 32 heads x 129 floats) and the stream-K
+    # state (table prefix sums + 2 slots x 16 rows for each of 4096 waves, outputs + LSE)
+    sk = lambda t, d: ((4 * (t + 1) + 255) // 256 * 256) + 2 * 4096 * 16 * d * 4 + 2 * 4096 * 16 * 4
+    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 4096) == max(8 * 64 * 32 * 129 * 4, sk(64, 128))
+    assert lib.pkv_attn_decode_workspace_bytes(64, 1, 32, 8, 128, 512) == sk(64, 128)
+    assert lib.pkv_attn_decode_workspace_bytes(256, 1, 64, 8, 128, 32768) == max(16 * 256 * 64 * 129 * 4,
+                                                                                sk(256, 128))
+    assert lib.pkv_attn_decode_workspace_bytes(0, 1, 64, 8, 128, 32768) == 0

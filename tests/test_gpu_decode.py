@@ -30,8 +30,16 @@ def _oracle_pools(case):
     return kp, vp
 
 
-def run_decode(case, out_dtype=torch.bfloat16, use_ws=True, q_override=None):
-    """Scatter the case's new tokens, then decode; returns (out, lse) numpy and the device pool."""
+def split_only_bytes(t, n, hq, d, max_len):
+    """Workspace that holds the key-split partials but not the stream-K state
+    (splits: chunks of >= 512 tokens, at most 16), so the split kernel runs."""
+    splits = min(16, max(1, -(-max_len // 512)))
+    return splits * t * n * hq * (d + 1) * 4 if splits > 1 else 0
+
+
+def run_decode(case, out_dtype=torch.bfloat16, use_ws="sk", q_override=None):
+    """Scatter the case's new tokens, then decode; returns (out, lse) numpy and the device pool.
+    use_ws: "sk" (full workspace: stream-K), "split" (key-split partials only) or "none"."""
     pool = pool_to_dev(case.pool)
     if case.slots is not None:
         pkv.pkv_scatter_slots(pool, to_dev(case.new_k), to_dev(case.new_v), to_dev(case.slots))
@@ -40,16 +48,18 @@ def run_decode(case, out_dtype=torch.bfloat16, use_ws=True, q_override=None):
     out = torch.full((t, n, hq, d), float("nan"), dtype=out_dtype, device=DEV)
     lse = torch.full((t, n, hq), float("nan"), dtype=torch.float32, device=DEV)
     ws = None
-    if use_ws:
+    if use_ws in ("sk", True):
         nb = pkv.pkv_attn_decode_workspace_bytes(t, n, hq, case.pool.num_kv_heads, d, case.max_kv_len)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    elif use_ws == "split":
+        ws = torch.empty(max(split_only_bytes(t, n, hq, d, case.max_kv_len), 16), dtype=torch.uint8, device=DEV)
     pkv.pkv_attn_decode(pool, q, to_dev(case.tables), to_dev(case.kv_lens), case.max_kv_len, case.sm_scale, out, lse,
                         ws)
     torch.cuda.synchronize()
     return as_f64(from_dev(out)), from_dev(lse).astype(np.float64), pool
 
 
-def check_decode(case, out_dtype=torch.bfloat16, use_ws=True, subset=None, q_override=None):
+def check_decode(case, out_dtype=torch.bfloat16, use_ws="sk", subset=None, q_override=None):
     note(f"decode {case.name} T={len(case.kv_lens)} n={case.rows_per_table} Hq={case.num_q_heads} "
          f"Hkv={case.pool.num_kv_heads} D={case.pool.head_dim} ps={case.pool.page_size} kv={case.pool.dtype} "
          f"max_len={case.max_kv_len} ws={use_ws} out={out_dtype}")
@@ -151,13 +161,25 @@ DECODE_CASES = [
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
-@pytest.mark.parametrize("use_ws", [True, False], ids=["split", "nosplit"])
+@pytest.mark.parametrize("use_ws", ["sk", "split", "none"])
 def test_decode_parity(case, use_ws):
     name, lens, hq, hkv, d, ps, n, kv = case
     c = W.make_decode_case(name, 31, 1031, len(lens), hq, hkv, d, ps, lens, kv_dtype=kv, rows_per_table=n,
                            new_per_seq=0 if kv == "fp8" else 1, extra_table_cols=2,
                            num_pool_pages=sum(math.ceil(L / ps) for L in lens) + 9)
     check_decode(c, use_ws=use_ws)
+
+
+def test_decode_stream_k_many_rows_with_empty_ones():
+    """Hundreds of table rows (some empty) so that chunk boundaries cut many
+    units and whole units fall inside one worker's chunk."""
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 300, size=300)
+    lens[::7] = 0
+    lens[5] = 4000
+    c = W.make_decode_case("many_rows", 81, 1081, len(lens), 8, 2, 128, 32, lens, new_per_seq=1)
+    check_decode(c, use_ws="sk")
+    check_decode(c, out_dtype=torch.float32, use_ws="sk")
 
 
 def test_decode_fp32_out_and_fp32_query_paths():
@@ -174,13 +196,14 @@ def test_decode_fp32_out_and_fp32_query_paths():
     assert_close(got_lse, ref_lse, "f32", "valu lse")
 
 
-def test_decode_page_permutation_gives_bit_identical_output():
+@pytest.mark.parametrize("use_ws", ["sk", "split"])
+def test_decode_page_permutation_gives_bit_identical_output(use_ws):
     lens = [1000, 37, 2048, 513]
     outs = []
     for perm_seed in (5, 6, 7):
         c = W.make_decode_case("perm", 51, perm_seed, len(lens), 32, 8, 128, 32, lens, num_pool_pages=400)
-        note(f"page permutation seed {perm_seed}")
-        got, got_lse, _ = run_decode(c)
+        note(f"page permutation seed {perm_seed} ws={use_ws}")
+        got, got_lse, _ = run_decode(c, use_ws=use_ws)
         outs.append((got, got_lse))
     for got, got_lse in outs[1:]:
         assert np.array_equal(got, outs[0][0]) and np.array_equal(got_lse, outs[0][1])

@@ -12,7 +12,7 @@ entries and lengths read, the scattered rows) over the measured step time.
 The other workloads (block-causal prefill, shared-prefix n-sample decode,
 long fp8 decode) are measured in the same run and reported under
 ``"workloads"``; each timed step there is bracketed by HIP events on the
-launch stream with a 512 MiB write between steps (outside the events) so
+launch stream with a 512 MiB read between steps (outside the events) so
 their working sets cannot stay in the 256 MiB Infinity Cache.
 
 ``roofline`` describes the dominant call of the headline (the decode), timed
@@ -75,13 +75,14 @@ def decode_bytes(kv_lens, page_size, hkv, d, kv_esize, n_rows_q, hq, q_esize, ou
 
 
 class Flusher:
-    """Writes 512 MiB between steps so the next step starts from HBM."""
+    """Reads 512 MiB between steps (a read, so no dirty lines are left to write
+    back) so the next step finds none of its inputs in the 256 MiB Infinity Cache."""
 
     def __init__(self, torch):
         self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
 
     def __call__(self):
-        self.buf.fill_(1)
+        self.buf.sum()
 
 
 def time_events(torch, step, reps, flush=None):

@@ -149,8 +149,10 @@ pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void
  *                float rounding, possibly slower).
  * Kernels: q bf16 with K/V bf16 or fp8 run on bf16 MFMA; q fp32 (any K/V
  * dtype) runs on the vector ALUs.  head_dim 64 or 128.
+ * sm_scale must be finite and > 0.
  * Errors: NULL pointers -> PKV_ERR_NULL; num_q_heads % num_kv_heads,
- * negative sizes, page_size < 16 -> PKV_ERR_SHAPE; unknown dtype ->
+ * negative sizes, sm_scale <= 0 -> PKV_ERR_SHAPE; page_size < 16 ->
+ * PKV_ERR_UNSUPPORTED; unknown dtype ->
  * PKV_ERR_DTYPE; other head_dim / dtype combinations or missing fp8 scales ->
  * PKV_ERR_UNSUPPORTED.
  */

@@ -165,7 +165,8 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
-  if (num_tables < 0 || rows_per_table < 1 || num_q_heads < 1 || table_stride < 1 || max_kv_len < 0)
+  if (num_tables < 0 || rows_per_table < 1 || num_q_heads < 1 || table_stride < 1 || max_kv_len < 0 ||
+      !(sm_scale > 0.f) || sm_scale > 3.0e38f)
     return PKV_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_kv_len > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;
@@ -281,7 +282,7 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
   if (batch < 0 || s_q < 0 || num_q_heads < 1 || table_stride < 1 || max_keys < 0 || causal_block_size < 0 ||
-      q_tok_stride < 0 || q_head_stride < 0)
+      q_tok_stride < 0 || q_head_stride < 0 || !(sm_scale > 0.f) || sm_scale > 3.0e38f)
     return PKV_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_keys > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;

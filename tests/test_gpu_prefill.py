@@ -1,0 +1,139 @@
+"""GPU parity of the block-causal paged prefill against the oracle.
+
+The new tokens are scattered from a packed QKV projection (strided K/V
+slices, padding rows skipped through negative slots) and the prefill reads the
+Q slice of the same tensor.  Dead rows of the last page, unowned pages and the
+table entries past each row's last page hold NaN, so any read outside the
+visible key set poisons the output."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import paged_kv_cache_slots_amd as pkv
+import workloads as W
+from gpu_util import DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(c, out_dtype=torch.bfloat16, qkv_override=None):
+    pool = pool_to_dev(c.pool)
+    qkv = to_dev(c.qkv if qkv_override is None else qkv_override)        # [B, S, Hq + 2 Hkv, D]
+    b, s_q, nh, d = qkv.shape
+    hq, hkv = c.num_q_heads, c.num_kv_heads
+    flat = qkv.view(b * s_q, nh, d)
+    pkv.pkv_scatter_slots(pool, flat[:, hq:hq + hkv], flat[:, hq + hkv:], to_dev(c.slots))
+    out = torch.full((b, s_q, hq, d), float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full((b, s_q, hq), float("nan"), dtype=torch.float32, device=DEV)
+    pkv.pkv_attn_prefill_block_causal(pool, qkv[:, :, :hq], to_dev(c.tables), to_dev(c.n_ctx), to_dev(c.seq_len),
+                                      c.causal_block_size, c.max_keys, c.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    return as_f64(from_dev(out)), from_dev(lse).astype(np.float64)
+
+
+def oracle_prefill(c, rows=None, qkv_override=None):
+    qkv = c.qkv if qkv_override is None else qkv_override
+    b, s_q, nh, d = qkv.shape
+    hq, hkv = c.num_q_heads, c.num_kv_heads
+    flat = qkv.reshape(b * s_q, nh, d)
+    kp = orc.scatter_slots(c.pool.k, flat[:, hq:hq + hkv], c.slots)
+    vp = orc.scatter_slots(c.pool.v, flat[:, hq + hkv:], c.slots)
+    return orc.attn_prefill_block_causal(kp, vp, qkv[:, :, :hq], c.tables, c.n_ctx, c.seq_len,
+                                         c.causal_block_size, c.sm_scale, kv_dtype=c.pool.dtype, rows_subset=rows)
+
+
+def check(c, out_dtype=torch.bfloat16, rows=None):
+    note(f"prefill {c.name} B={c.qkv.shape[0]} s_q={c.s_q} seq={list(c.seq_len)} n_ctx={list(c.n_ctx)} "
+         f"Hq={c.num_q_heads} Hkv={c.num_kv_heads} D={c.qkv.shape[-1]} ps={c.pool.page_size} "
+         f"cbs={c.causal_block_size} out={out_dtype}")
+    got, got_lse = run_prefill(c, out_dtype)
+    ref, ref_lse = oracle_prefill(c, rows)
+    if rows is None:
+        sel = (slice(None),)
+        g, gl, r, rl = got, got_lse, ref, ref_lse
+    else:
+        bi = np.array([x[0] for x in rows])
+        ii = np.array([x[1] for x in rows])
+        g, gl, r, rl = got[bi, ii], got_lse[bi, ii], ref[bi, ii], ref_lse[bi, ii]
+    assert_close(g, r, "bf16", f"{c.name} out")
+    assert_close(gl, rl, "bf16", f"{c.name} lse")
+    # padding rows are exactly zero with LSE -inf, everywhere
+    for bb in range(got.shape[0]):
+        pad = slice(int(c.seq_len[bb]), None)
+        assert np.all(got[bb, pad] == 0) and np.all(np.isneginf(got_lse[bb, pad]))
+    assert not np.any(np.isnan(got))
+
+
+SMALL = [
+    # name, B, s_q, seq_lens, n_ctx, Hq, Hkv, D, ps, cbs
+    ("one_block_d128", 1, 200, [200], [300], 4, 4, 128, 32, 0),
+    ("padded_gqa_d128", 2, 150, [131, 150], [64, 5], 8, 2, 128, 32, 0),
+    ("blocks_of_37", 1, 260, [250], [97], 2, 2, 128, 16, 37),
+    ("causal_cbs1", 1, 70, [70], [0], 2, 1, 64, 16, 1),
+    ("blocks_64_ps64", 2, 300, [300, 257], [640, 0], 4, 2, 64, 64, 64),
+    ("no_context", 1, 129, [129], [0], 3, 3, 128, 32, 100),
+    ("all_padding_batch", 2, 40, [0, 33], [12, 40], 2, 2, 128, 32, 8),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[s[0] for s in SMALL])
+def test_prefill_small_exhaustive(case):
+    name, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs = case
+    c = W.make_prefill_case(name, 91, 1091, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs,
+                            num_pool_pages=sum(math.ceil((s + x) / ps) for s, x in zip(seqs, ctxs)) + 7,
+                            extra_table_cols=2)
+    check(c)
+
+
+def test_prefill_fp32_output():
+    c = W.make_prefill_case("f32out", 92, 1092, 1, 140, [133], [50], 4, 2, 128, 32, 20, extra_table_cols=1)
+    check(c, out_dtype=torch.float32)
+
+
+def test_prefill_stamped_values_reveal_visible_key_counts():
+    """q = 0 gives equal scores, so output dim 0 is the mean of the visible
+    keys' stamps V[key][0] = key: (count - 1) / 2 exactly."""
+    c = W.make_prefill_case("stamped", 93, 1093, 1, 100, [90], [37], 2, 2, 128, 16, 13, extra_table_cols=1)
+    qkv = c.qkv.copy()
+    qkv[:, :, :2] = 0                                                    # q = 0 (bf16 zero)
+    stamps = np.zeros((1, 100, 2, 128), dtype=np.float32)
+    stamps[0, :, :, 0] = (37 + np.arange(100))[:, None]                 # new tokens' stamps
+    qkv[:, :, 4:] = W.to_storage(stamps, "bf16")
+    ctx_stamp = np.zeros_like(as_f64(c.pool.v), dtype=np.float32)
+    for j in range(math.ceil(37 / 16)):
+        for r in range(16):
+            if j * 16 + r < 37:
+                ctx_stamp[c.tables[0, j], r, :, 0] = j * 16 + r
+    v = c.pool.v.copy()
+    owned = c.tables[0, :math.ceil(37 / 16)]
+    v[owned] = np.where(np.isnan(as_f64(v[owned])), v[owned], W.to_storage(ctx_stamp[owned], "bf16"))
+    c.pool.v = v
+    got, _ = run_prefill(c, torch.float32, qkv_override=qkv)
+    for i in range(100):
+        cnt = orc.prefill_visible_keys(i, 37, 90, 13)
+        if cnt == 0:
+            assert np.all(got[0, i] == 0)
+        else:
+            np.testing.assert_allclose(got[0, i, :, 0], (cnt - 1) / 2.0, rtol=1e-6)
+
+
+def test_prefill_page_permutation_bit_identical():
+    outs = []
+    for perm_seed in (11, 12):
+        c = W.make_prefill_case("perm", 94, perm_seed, 1, 300, [290], [700], 4, 4, 128, 32, 50,
+                                num_pool_pages=80)
+        note(f"prefill permutation {perm_seed}")
+        outs.append(run_prefill(c))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("cbs", [1560, 390])
+def test_prefill_config3_sampled(cbs):
+    c = W.config3(causal_block_size=cbs)
+    rows = sorted({(0, i) for i in [0, 1, 127, 128, 389, 390, 391, 779, 780, 1000, 1169, 1170, 1535, 1536,
+                                    1559, 1560, 1567]})
+    check(c, rows=rows)

@@ -168,13 +168,16 @@ def run_config3(torch, pkv, W, flush):
     tables, n_ctx, seq = to_dev(case.tables, torch), to_dev(case.n_ctx, torch), to_dev(case.seq_len, torch)
     out = torch.empty((1, s_q, hq, d), dtype=torch.bfloat16, device="cuda:0")
     q = qkv[:, :, :hq]
+    # workspace for the split leftover query tiles (contents ignored)
+    ws = torch.empty(max(16, pkv.pkv_attn_prefill_workspace_bytes(1, s_q, hq, hkv, d, case.max_keys)),
+                     dtype=torch.uint8, device="cuda:0")
 
     def scatter():
         pkv.pkv_scatter_slots(pool, k_src, v_src, slots)
 
     def prefill():
         pkv.pkv_attn_prefill_block_causal(pool, q, tables, n_ctx, seq, case.causal_block_size, case.max_keys,
-                                          case.sm_scale, out)
+                                          case.sm_scale, out, None, ws)
 
     try:
         scatter()

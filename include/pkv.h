@@ -192,8 +192,14 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
  *                      out_dtype PKV_BF16 or PKV_F32; rows i >= seq_len are 0.
  *   out_lse            NULL or float [batch, s_q, num_q_heads]; -inf for
  *                      padding rows.
- *   workspace          NULL or scratch of pkv_attn_prefill_workspace_bytes
- *                      (for key splits); NULL runs unsplit.
+ *   workspace          NULL, or device scratch of at least
+ *                      pkv_attn_prefill_workspace_bytes(...) bytes (a fixed
+ *                      65 MiB), 256-byte aligned, contents ignored.  With
+ *                      it the query tiles left over after the last full
+ *                      round of a persistent grid are split along the keys
+ *                      and merged by a second kernel on the same stream; with
+ *                      NULL (or too small / misaligned) they run whole.  Two
+ *                      calls in flight at once need two workspaces.
  * Kernel: bf16 MFMA; K/V bf16; head_dim 128 or 64.
  * Errors: as pkv_attn_decode.
  */

@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "pkv_internal.hpp"
 
 namespace {
@@ -266,8 +266,9 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
 // ---------------------------------------------------------------------------
 size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_keys) {
-  (void)batch; (void)s_q; (void)num_q_heads; (void)num_kv_heads; (void)head_dim; (void)max_keys;
-  return 0;
+  (void)num_kv_heads; (void)head_dim; (void)max_keys;
+  if (batch <= 0 || s_q <= 0 || num_q_heads <= 0) return 0;
+  return (size_t)(2 * (int64_t)kMaxPrefillWorkgroups * (int64_t)prefill_slot_bytes());
 }
 
 pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
@@ -277,7 +278,6 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
                                          int32_t max_keys, float sm_scale, void* out, pkv_dtype out_dtype,
                                          float* out_lse, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream) {
-  (void)workspace; (void)workspace_bytes;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
@@ -319,7 +319,12 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   p.q_tiles = 0;
   p.out_bf16 = out_dtype == PKV_BF16;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  return launch_prefill_mfma(p, D, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  p.ws_o = nullptr;
+  const int cus = device_cu_count();
+  const size_t need = pkv_attn_prefill_workspace_bytes(batch, s_q, num_q_heads, pool->num_kv_heads, D, max_keys);
+  if (need > 0 && cus > 0 && workspace && aligned(workspace, 256) && workspace_bytes >= need)
+    p.ws_o = static_cast<float*>(workspace);
+  return launch_prefill_mfma(p, D, cus, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------

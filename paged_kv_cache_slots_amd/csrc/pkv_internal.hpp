@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 
 namespace pkv {
 
@@ -16,6 +16,11 @@ enum ElemType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 // state rows in the workspace (2 slots x 16 rows per wave of every worker).
 constexpr int kMaxSkTables = 8192;
 constexpr int kMaxSkWaves = 4096;
+
+// Prefill: workgroups of the persistent grid (2 partial-state slots each) and
+// the most leftover units an XCD splits along the keys.
+constexpr int kMaxPrefillWorkgroups = 512;
+constexpr int kMaxTailUnits = 64;
 
 struct ScatterParams {
   const uint8_t* src_k;
@@ -89,6 +94,7 @@ struct PrefillParams {
   const int32_t* seq_len;
   void* out;
   float* out_lse;
+  float* ws_o;                // stream-K partial states (NULL: leftover units run whole)
   int64_t page_stride;
   int64_t q_tok_stride;
   int64_t q_head_stride;
@@ -112,6 +118,8 @@ int sk_waves_per_worker(int rows_per_unit);
 hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
-hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
+int64_t prefill_units(int32_t batch, int32_t s_q, int32_t num_q_heads);
+size_t prefill_slot_bytes();
 
 }  // namespace pkv

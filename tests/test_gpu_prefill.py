@@ -20,17 +20,25 @@ from gpu_util import DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(c, out_dtype=torch.bfloat16, qkv_override=None):
+def run_prefill(c, out_dtype=torch.bfloat16, qkv_override=None, use_ws=True, repeat=1):
+    """Scatter the new tokens, then prefill (``repeat`` times on one workspace,
+    which starts as NaN bytes: its contents must not matter)."""
     pool = pool_to_dev(c.pool)
     qkv = to_dev(c.qkv if qkv_override is None else qkv_override)        # [B, S, Hq + 2 Hkv, D]
     b, s_q, nh, d = qkv.shape
     hq, hkv = c.num_q_heads, c.num_kv_heads
     flat = qkv.view(b * s_q, nh, d)
     pkv.pkv_scatter_slots(pool, flat[:, hq:hq + hkv], flat[:, hq + hkv:], to_dev(c.slots))
-    out = torch.full((b, s_q, hq, d), float("nan"), dtype=out_dtype, device=DEV)
-    lse = torch.full((b, s_q, hq), float("nan"), dtype=torch.float32, device=DEV)
-    pkv.pkv_attn_prefill_block_causal(pool, qkv[:, :, :hq], to_dev(c.tables), to_dev(c.n_ctx), to_dev(c.seq_len),
-                                      c.causal_block_size, c.max_keys, c.sm_scale, out, lse)
+    ws = None
+    if use_ws:
+        nb = pkv.pkv_attn_prefill_workspace_bytes(b, s_q, hq, hkv, d, c.max_keys)
+        ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=DEV)
+    for _ in range(repeat):
+        out = torch.full((b, s_q, hq, d), float("nan"), dtype=out_dtype, device=DEV)
+        lse = torch.full((b, s_q, hq), float("nan"), dtype=torch.float32, device=DEV)
+        pkv.pkv_attn_prefill_block_causal(pool, qkv[:, :, :hq], to_dev(c.tables), to_dev(c.n_ctx),
+                                          to_dev(c.seq_len), c.causal_block_size, c.max_keys, c.sm_scale, out, lse,
+                                          ws)
     torch.cuda.synchronize()
     return as_f64(from_dev(out)), from_dev(lse).astype(np.float64)
 
@@ -46,11 +54,11 @@ def oracle_prefill(c, rows=None, qkv_override=None):
                                          c.causal_block_size, c.sm_scale, kv_dtype=c.pool.dtype, rows_subset=rows)
 
 
-def check(c, out_dtype=torch.bfloat16, rows=None):
+def check(c, out_dtype=torch.bfloat16, rows=None, use_ws=True):
     note(f"prefill {c.name} B={c.qkv.shape[0]} s_q={c.s_q} seq={list(c.seq_len)} n_ctx={list(c.n_ctx)} "
          f"Hq={c.num_q_heads} Hkv={c.num_kv_heads} D={c.qkv.shape[-1]} ps={c.pool.page_size} "
-         f"cbs={c.causal_block_size} out={out_dtype}")
-    got, got_lse = run_prefill(c, out_dtype)
+         f"cbs={c.causal_block_size} out={out_dtype} ws={use_ws}")
+    got, got_lse = run_prefill(c, out_dtype, use_ws=use_ws, repeat=2 if use_ws else 1)
     ref, ref_lse = oracle_prefill(c, rows)
     if rows is None:
         sel = (slice(None),)
@@ -80,13 +88,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("use_ws", [True, False], ids=["stream_k", "per_unit"])
 @pytest.mark.parametrize("case", SMALL, ids=[s[0] for s in SMALL])
-def test_prefill_small_exhaustive(case):
+def test_prefill_small_exhaustive(case, use_ws):
     name, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs = case
     c = W.make_prefill_case(name, 91, 1091, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs,
                             num_pool_pages=sum(math.ceil((s + x) / ps) for s, x in zip(seqs, ctxs)) + 7,
                             extra_table_cols=2)
-    check(c)
+    check(c, use_ws=use_ws)
 
 
 def test_prefill_fp32_output():
@@ -131,9 +140,18 @@ def test_prefill_page_permutation_bit_identical():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("use_ws", [True, False], ids=["stream_k", "per_unit"])
 @pytest.mark.parametrize("cbs", [1560, 390])
-def test_prefill_config3_sampled(cbs):
+def test_prefill_config3_sampled(cbs, use_ws):
     c = W.config3(causal_block_size=cbs)
     rows = sorted({(0, i) for i in [0, 1, 127, 128, 389, 390, 391, 779, 780, 1000, 1169, 1170, 1535, 1536,
                                     1559, 1560, 1567]})
-    check(c, rows=rows)
+    check(c, rows=rows, use_ws=use_ws)
+
+
+def test_prefill_many_units_stream_k():
+    """Many small units over two batches: chunk boundaries cut units at many
+    places and some units fall whole inside one chunk."""
+    c = W.make_prefill_case("many_units", 95, 1095, 2, 700, [650, 333], [1200, 77], 16, 4, 128, 32, 100,
+                            extra_table_cols=1)
+    check(c, rows=[(0, i) for i in (0, 99, 100, 255, 256, 649, 650, 699)] + [(1, i) for i in (0, 200, 332, 333)])

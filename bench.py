@@ -1,6 +1,6 @@
 """Benchmark of the paged K/V-cache path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs 2,3,4,5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,shared,fp8] [--no-cpu-baseline]
 
 Prints ONE JSON line.  The headline workload is the bf16 GQA decode (64
 sequences, lengths uniform in [512, 4096], 32 q / 8 kv heads of 128, 32-token
@@ -38,19 +38,56 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
+# HBM byte counters of the decode call, taken by separate rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) and scaled by what the same counters read for a
+# copy of known size.  Valid only while the decode sources hash to the value
+# recorded with them; otherwise ``roofline.traffic`` is null.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa_bf16_hbm_counters.txt")
+DECODE_SOURCES = ["paged_kv_cache_slots_amd/csrc/decode.hip", "paged_kv_cache_slots_amd/csrc/pkv_device.hpp",
+                  "paged_kv_cache_slots_amd/csrc/pkv_internal.hpp", "paged_kv_cache_slots_amd/csrc/pkv_api.hip"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="3,4,5", help="secondary workloads to run (comma list of 3,4,5 or none)")
+    ap.add_argument("--workloads", default="prefill,shared,fp8",
+                    help="secondary workloads to run: comma list of prefill, shared, fp8 (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (calibrates the HBM byte counters) and exit")
     return ap.parse_args()
 
 
 # ----------------------------------------------------------------------------- helpers
+
+def decode_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it is missing or was taken on other decode sources."""
+    try:
+        kv = {}
+        with open(COUNTERS_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != decode_sources_sha256():
+            return None
+        return int(kv["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def to_dev(a, torch):
     a = np.ascontiguousarray(a)
@@ -120,7 +157,7 @@ def setup_decode_case(case, torch, pkv):
 
 
 def run_headline(args, torch, pkv, W):
-    case = W.config2()
+    case = W.gqa_bf16_decode()
     dev = setup_decode_case(case, torch, pkv)
     hkv, d = case.pool.num_kv_heads, case.pool.head_dim
     t, n, hq, _ = case.q.shape
@@ -156,8 +193,8 @@ def run_headline(args, torch, pkv, W):
 
 # ----------------------------------------------------------------------------- secondary workloads
 
-def run_config3(torch, pkv, W, flush):
-    case = W.config3()
+def run_prefill(torch, pkv, W, flush):
+    case = W.block_causal_prefill()
     pool = pkv.Pool(to_dev(case.pool.k, torch), to_dev(case.pool.v, torch))
     qkv = to_dev(case.qkv, torch)                       # [1, S, Hq + 2 Hkv, D]
     hq, hkv, d = case.num_q_heads, case.num_kv_heads, qkv.shape[-1]
@@ -203,8 +240,8 @@ def run_config3(torch, pkv, W, flush):
             "scatter_gbs": scat_bytes / (smed * 1e-3) / 1e9, "scatter_plus_prefill_ms": both}
 
 
-def run_config4(torch, pkv, W, flush):
-    c = W.config4()
+def run_shared_prefix(torch, pkv, W, flush):
+    c = W.shared_prefix_decode()
     pool = pkv.Pool(to_dev(c.pool.k, torch), to_dev(c.pool.v, torch))
     new_k, new_v, slots = to_dev(c.new_k, torch), to_dev(c.new_v, torch), to_dev(c.slots, torch)
     n_rows, hq, d, hkv = c.q.shape[0], c.num_q_heads, c.pool.head_dim, c.pool.num_kv_heads
@@ -255,8 +292,8 @@ def run_config4(torch, pkv, W, flush):
             "unshared_mb": (decode_bytes(c.full_lens, 32, hkv, d, 2, n_rows, hq, 2, 2, False, False) + scat) / 1e6}
 
 
-def run_config5(torch, pkv, W, flush):
-    c = W.config5()
+def run_long_fp8(torch, pkv, W, flush):
+    c = W.long_fp8_decode()
     dev = setup_decode_case(c, torch, pkv)
     t, n, hq, d = c.q.shape
     hkv = c.pool.num_kv_heads
@@ -279,30 +316,31 @@ def run_config5(torch, pkv, W, flush):
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(case, seconds):
-    """Time the float64 oracle (one BLAS thread) on the headline batch's first
-    tables until about ``seconds`` of CPU work; report the same algorithmic
-    bytes per second as the GPU figure."""
+    """Time the float64 oracle (one BLAS thread) on whole headline steps
+    (scatter of the new tokens + decode of all 64 sequences), repeated until
+    about ``seconds`` of CPU work; report the same algorithmic bytes per
+    second as the GPU figure."""
     from threadpoolctl import threadpool_limits
 
     import oracle as orc
 
-    kp = orc.scatter_slots(case.pool.k, case.new_k, case.slots)
-    vp = orc.scatter_slots(case.pool.v, case.new_v, case.slots)
     hkv, d = case.pool.num_kv_heads, case.pool.head_dim
-    done, spent = [], 0.0
+    t_rows, n, hq, _ = case.q.shape
+    step_bytes = (decode_bytes(case.kv_lens, case.pool.page_size, hkv, d, 2, t_rows * n, hq, 2, 2, False, False)
+                  + 2 * 2 * len(case.slots) * hkv * d * 2 + len(case.slots) * 8)
+    steps, spent = 0, 0.0
     with threadpool_limits(limits=1):
-        for t in range(len(case.kv_lens)):
+        while spent < seconds:
             t0 = time.perf_counter()
-            orc.attn_decode(kp, vp, case.q, case.tables, case.kv_lens, case.sm_scale, tables_subset=[t])
+            kp = orc.scatter_slots(case.pool.k, case.new_k, case.slots)
+            vp = orc.scatter_slots(case.pool.v, case.new_v, case.slots)
+            orc.attn_decode(kp, vp, case.q, case.tables, case.kv_lens, case.sm_scale)
             spent += time.perf_counter() - t0
-            done.append(t)
-            if spent >= seconds:
-                break
-    lens = case.kv_lens[done]
-    nbytes = decode_bytes(lens, case.pool.page_size, hkv, d, 2, len(done), case.num_q_heads, 2, 2, False, False)
-    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle decode of {len(done)} of the 64 sequences ({int(lens.sum())} keys, "
-                      f"{nbytes / 1e6:.1f} MB algorithmic) after its own scatter; {spent:.1f} s on one thread"}
+            steps += 1
+    return {"value": steps * step_bytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole steps of the headline batch (scatter of 64 new tokens + float64 decode of "
+                      f"all 64 sequences, {int(case.kv_lens.sum())} keys, {step_bytes / 1e6:.1f} MB algorithmic "
+                      f"per step) in {spent:.1f} s on one thread"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -320,6 +358,22 @@ def main():
 
     pkv.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe > 0:
+        # a copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch against
+        # MIB MiB each give the counters' scale on this chip
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        ms = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src)
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        print(json.dumps({"copy_probe_mib": args.copy_probe, "median_ms": float(np.median(ms)),
+                          "gbs_read_plus_write": 2 * (args.copy_probe << 20) / (float(np.median(ms)) * 1e-3) / 1e9}))
+        return
     case, h = run_headline(args, torch, pkv, W)
     value = h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9
     achieved = h["dec_bytes"] / (h["decode_ms"] * 1e-3) / 1e9
@@ -334,16 +388,18 @@ def main():
                    "global_batch": 64, "seq_len": int(case.max_kv_len), "total_keys": int(case.kv_lens.sum()),
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "pkv_attn_decode call (decode kernel + split merge kernel)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
         "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],
     }
     workloads = {}
     flush = Flusher(torch)
-    for cfg in [c for c in args.configs.split(",") if c.strip() and c != "none"]:
-        fn = {"3": run_config3, "4": run_config4, "5": run_config5}[cfg.strip()]
-        workloads[f"config{cfg.strip()}"] = fn(torch, pkv, W, flush)
+    runners = {"prefill": ("block_causal_prefill", run_prefill), "shared": ("shared_prefix_decode", run_shared_prefix),
+               "fp8": ("long_fp8_decode", run_long_fp8)}
+    for name in [w.strip() for w in args.workloads.split(",") if w.strip() and w.strip() != "none"]:
+        key, fn = runners[name]
+        workloads[key] = fn(torch, pkv, W, flush)
         torch.cuda.empty_cache()
     if workloads:
         result["workloads"] = workloads

@@ -583,8 +583,12 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
 
 // Joins the partial states of units cut by chunk boundaries, and writes the
 // zero output / -inf LSE of table rows with no keys.  One thread per (row,
-// 4 dims) of every unit; units a single worker finished are skipped.
+// 4 dims) of every unit; units a single worker finished are skipped.  The
+// loads of each stage go out together (prefix sums, then the pieces' LSEs,
+// then LSEs and values, 4 pieces at a time), so a merge costs three memory
+// round trips rather than one per piece.
 __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_per_worker, int head_dim) {
+  constexpr int PB = 4;
   const int D = head_dim;
   const int chunks = D >> 2;
   const int R = p.rows_per_table * p.group;
@@ -601,32 +605,49 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_pe
   const int rg = r / rows_w;
   const int HR = p.num_kv_heads * p.row_groups;
   const int T = p.num_tables;
-  const int64_t N = (int64_t)p.ws_cum[T] * HR;
+  const int32_t cum_all = p.ws_cum[T], cum_t = p.ws_cum[t], cum_t1 = p.ws_cum[t + 1];
+  const int64_t N = (int64_t)cum_all * HR;
   const int64_t C = (N + p.n_workers - 1) / p.n_workers;
-  const int tiles = p.ws_cum[t + 1] - p.ws_cum[t];
+  const int tiles = cum_t1 - cum_t;
   int qi;
   int64_t qrow;
   row_of(p, t, g, r, qi, qrow);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lse_out = kNegInf;
   if (tiles > 0) {
-    const int64_t F = (int64_t)p.ws_cum[t] * HR + (int64_t)(g * p.row_groups + rg) * tiles;
+    const int64_t F = (int64_t)cum_t * HR + (int64_t)(g * p.row_groups + rg) * tiles;
     const int64_t w0 = F / C, w1 = (F + tiles - 1) / C;
     if (w0 == w1) return;   // finished by one worker
     const int row_in = r - rg * rows_w;
-    float m = kNegInf;
-    for (int64_t w = w0; w <= w1; ++w) {
+    auto slot_row = [&](int64_t w) {
       const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
-      m = fmaxf(m, p.ws_lse[slot * rows_w + row_in]);
+      return slot * rows_w + row_in;
+    };
+    float m = kNegInf;
+    for (int64_t w = w0; w <= w1; w += PB) {
+      float l[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) l[j] = w + j <= w1 ? p.ws_lse[slot_row(w + j)] : kNegInf;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) m = fmaxf(m, l[j]);
     }
     if (m != kNegInf) {
       float wsum = 0.f;
-      for (int64_t w = w0; w <= w1; ++w) {
-        const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
-        const float lw = p.ws_lse[slot * rows_w + row_in];
-        const float f = fast_exp2((lw - m) * kLog2e);
-        if (f > 0.f) {
-          acc += f * *reinterpret_cast<const f32x4*>(p.ws_o + (slot * rows_w + row_in) * D + 4 * ch);
+      for (int64_t w = w0; w <= w1; w += PB) {
+        float l[PB];
+        f32x4 v[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const bool ok = w + j <= w1;
+          const int64_t sr = slot_row(ok ? w + j : w1);
+          l[j] = ok ? p.ws_lse[sr] : kNegInf;
+          v[j] = *reinterpret_cast<const f32x4*>(p.ws_o + sr * D + 4 * ch);
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          // every piece holds keys, so its state is finite; padding entries weigh 0
+          const float f = l[j] == kNegInf ? 0.f : fast_exp2((l[j] - m) * kLog2e);
+          acc += f * v[j];
           wsum += f;
         }
       }

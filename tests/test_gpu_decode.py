@@ -80,16 +80,16 @@ def check_decode(case, out_dtype=torch.bfloat16, use_ws="sk", subset=None, q_ove
 # --------------------------------------------------------------------------- scatter
 
 
-def test_config1_scatter_is_bit_exact_then_fp32_decode():
-    c = W.config1()
-    note("config1 scatter + fp32 decode")
+def test_tiny_fp32_scatter_is_bit_exact_then_fp32_decode():
+    c = W.tiny_fp32_decode()
+    note("tiny_fp32_decode scatter + fp32 decode")
     got, got_lse, pool = run_decode(c, out_dtype=torch.float32)
     kp, vp = _oracle_pools(c)
     assert np.array_equal(from_dev(pool.k).view(np.uint32), kp.view(np.uint32))
     assert np.array_equal(from_dev(pool.v).view(np.uint32), vp.view(np.uint32))
     ref, ref_lse = orc.attn_decode(kp, vp, c.q, c.tables, c.kv_lens, c.sm_scale, kv_dtype="f32")
-    assert_close(got, ref, "f32", "config1 out")
-    assert_close(got_lse, ref_lse, "f32", "config1 lse")
+    assert_close(got, ref, "f32", "tiny_fp32_decode out")
+    assert_close(got_lse, ref_lse, "f32", "tiny_fp32_decode lse")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
@@ -134,7 +134,7 @@ def test_scatter_variants_bit_exact(dtype, variant):
 
 
 def test_scatter_empty_is_noop():
-    c = W.config1()
+    c = W.tiny_fp32_decode()
     pool = pool_to_dev(c.pool)
     before = from_dev(pool.k).copy()
     pkv.pkv_scatter_slots(pool, to_dev(c.new_k), to_dev(c.new_v), to_dev(c.slots[:0]))
@@ -232,16 +232,16 @@ def test_decode_peaked_newest_key_dominates():
             np.testing.assert_allclose(got[t, 0, h], vnew[t, h // 4], atol=3e-2)
 
 
-def test_full_size_config2_sampled():
-    c = W.config2()
+def test_full_size_gqa_bf16_decode_sampled():
+    c = W.gqa_bf16_decode()
     rng = np.random.default_rng(0)
     subset = sorted(set(rng.choice(len(c.kv_lens), 8, replace=False).tolist()) |
                     {int(np.argmax(c.kv_lens)), int(np.argmin(c.kv_lens))})
     check_decode(c, subset=subset)
 
 
-def test_full_size_config5_sampled():
-    c = W.config5()
+def test_full_size_long_fp8_decode_sampled():
+    c = W.long_fp8_decode()
     rng = np.random.default_rng(1)
     subset = sorted(set(rng.choice(len(c.kv_lens), 5, replace=False).tolist()) | {int(np.argmax(c.kv_lens))})
     check_decode(c, subset=subset)

@@ -72,12 +72,12 @@ def _shared_prefix_flow(c, check_unshared=True):
             None if unshared is None else as_f64(from_dev(unshared))[:, 0])
 
 
-@pytest.mark.parametrize("size", ["small", "config4"])
+@pytest.mark.parametrize("size", ["small", "shared_prefix_decode"])
 def test_shared_prefix_merge_equals_full_attention(size):
     if size == "small":
         c = W.make_shared_prefix_case("sp_small", 71, 1071, 3, 5, 256, (1, 70), 16, 4, 128, 32, 128)
     else:
-        c = W.config4()
+        c = W.shared_prefix_decode()
     note(f"shared prefix flow {size}")
     got, got_lse, unshared = _shared_prefix_flow(c)
     kp = orc.scatter_slots(c.pool.k, c.new_k, c.slots)

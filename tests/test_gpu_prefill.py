@@ -142,8 +142,8 @@ def test_prefill_page_permutation_bit_identical():
 
 @pytest.mark.parametrize("use_ws", [True, False], ids=["stream_k", "per_unit"])
 @pytest.mark.parametrize("cbs", [1560, 390])
-def test_prefill_config3_sampled(cbs, use_ws):
-    c = W.config3(causal_block_size=cbs)
+def test_prefill_full_size_sampled(cbs, use_ws):
+    c = W.block_causal_prefill(causal_block_size=cbs)
     rows = sorted({(0, i) for i in [0, 1, 127, 128, 389, 390, 391, 779, 780, 1000, 1169, 1170, 1535, 1536,
                                     1559, 1560, 1567]})
     check(c, rows=rows, use_ws=use_ws)

@@ -5,8 +5,8 @@ import numpy as np
 import workloads as W
 
 
-def test_config1_layout():
-    c = W.config1()
+def test_tiny_fp32_decode_layout():
+    c = W.tiny_fp32_decode()
     assert c.pool.k.shape == (32, 32, 4, 64) and c.pool.k.dtype == np.float32
     assert c.tables.shape == (2, 10) and list(c.kv_lens) == [256, 256]
     assert c.new_k.shape == (4, 4, 64) and len(c.slots) == 4
@@ -24,7 +24,7 @@ def test_config1_layout():
 
 
 def test_seeded_inputs_are_reproducible():
-    a, b = W.config1(), W.config1()
+    a, b = W.tiny_fp32_decode(), W.tiny_fp32_decode()
     assert np.array_equal(a.q, b.q) and np.array_equal(a.tables, b.tables)
     assert np.array_equal(a.pool.k, b.pool.k, equal_nan=True)
 

@@ -246,14 +246,14 @@ def make_decode_case(name, seed, perm_seed, num_tables, num_q_heads, num_kv_head
                       1.0 / math.sqrt(head_dim), new_k, new_v, slots, poison_page)
 
 
-def config1(seed=1):
+def tiny_fp32_decode(seed=1):
     """Tiny fp32 decode: 2 sequences of 256 keys (254 resident + 2 new), 4/4
     heads of 64, 32-token pages, a 32-page pool randomly permuted."""
     return make_decode_case("tiny_fp32_decode", seed, 1000 + seed, 2, 4, 4, 64, 32, [256, 256],
                             num_pool_pages=32, kv_dtype="f32", new_per_seq=2, extra_table_cols=2)
 
 
-def config2(seed=2, batch=64, len_range=(512, 4096), num_pool_pages=16384):
+def gqa_bf16_decode(seed=2, batch=64, len_range=(512, 4096), num_pool_pages=16384):
     """bf16 GQA decode: 64 sequences, lengths uniform in [512, 4096], 32 q /
     8 kv heads of 128, 32-token pages shuffled across a 16k-page pool, one new
     token per sequence scattered before attention."""
@@ -263,7 +263,7 @@ def config2(seed=2, batch=64, len_range=(512, 4096), num_pool_pages=16384):
                             num_pool_pages=num_pool_pages, kv_dtype="bf16", new_per_seq=1)
 
 
-def config5(seed=5, batch=256, len_range=(1024, 32768)):
+def long_fp8_decode(seed=5, batch=256, len_range=(1024, 32768)):
     """Large fp8 decode: 256 sequences, lengths log-uniform in [1024, 32768],
     64 q / 8 kv heads of 128, e4m3fn K/V with a float scale per (page, kv
     head), bf16 queries and outputs, pages randomly permuted."""
@@ -341,7 +341,7 @@ def make_shared_prefix_case(name, seed, perm_seed, groups, samples, prefix_len, 
                             full_tables, (tails + prefix_len).astype(np.int32), new_k, new_v, slots, poison_page)
 
 
-def config4(seed=4, groups=8, samples=16, prefix_len=2048, tail_range=(1, 512), num_pool_pages=4096):
+def shared_prefix_decode(seed=4, groups=8, samples=16, prefix_len=2048, tail_range=(1, 512), num_pool_pages=4096):
     """Shared-prefix n-sample decode: 8 prompts x 16 samples, 2048 shared
     prefix tokens per prompt, private tails uniform in [1, 512], 32 q / 8 kv
     heads of 128, bf16, 32-token pages in a 4096-page pool."""
@@ -424,7 +424,7 @@ def make_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, num_q
                        poison_page)
 
 
-def config3(seed=3, causal_block_size=1560):
+def block_causal_prefill(seed=3, causal_block_size=1560):
     """bf16 block-causal prefill (video-generation style): 24 heads of 128,
     32-token pages, pinned prefix 1024 + rolling history 4096 + a current block
     of 1560 real queries padded to 1568 rows; every query sees the prefix, the

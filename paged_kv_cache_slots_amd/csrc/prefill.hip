@@ -12,10 +12,10 @@
 // seq_len)) of its table row; rows i >= seq_len get o = 0, lse = -inf.
 //
 // Work unit: 128 query rows of one query head (a q-tile).  Its keys are walked
-// in tiles of 64.  A workgroup has 8 waves: 4 row blocks of 32 query rows x 2
-// key halves (keys 0-31 / 32-63 of every tile).  Both waves of a row block
-// share a SIMD and keep their own softmax state; they are joined at the end
-// of a segment with the log-sum-exp merge.
+// in tiles of 64.  A workgroup has 8 waves (two per SIMD): 4 row blocks of 32
+// query rows x 2 key halves (keys 0-31 / 32-63 of every tile).  Both waves of
+// a row block keep their own softmax state; they are joined at the end of a
+// segment with the log-sum-exp merge.
 //
 //   * S^T[key][q] = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS,
 //     B = Q held in registers): each lane owns one query row and 16 keys.
@@ -23,13 +23,21 @@
 //     bf16 (no shuffle); V^T operands come straight from the row-major V tile
 //     through ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-dim
 //     block and gets it transposed), so staging never transposes.
-//   * Software pipeline: the QK^T MFMAs of tile t+1 are issued before the
-//     softmax of tile t, so matrix cores and vector ALUs overlap within a wave.
-//     K runs one tile ahead of V through two LDS buffers each; one barrier per
-//     tile.  Global loads for the next stage are issued a full tile ahead.
-//   * Loads never branch: keys at or past the unit's last visible key read a
-//     valid row and are replaced by zeros, so dead page slots and table
-//     entries past the last page never reach a product (and are never read).
+//   * K/V tiles go from HBM to LDS by LDS-DMA (buffer loads that write LDS
+//     directly, no staging registers), three stages each, two tiles ahead.
+//     Rows are XOR-swizzled in 16-byte chunks instead of padded (the DMA
+//     writes 1 KiB runs), keeping both operand read patterns conflict-free.
+//   * Software pipeline of a wave, per tile t: exp of S(t) -> P(t); QK^T of
+//     tile t+1; PV of tile t-1.  The two MFMA chains do not depend on the
+//     vector work, so matrix cores and vector ALUs overlap within a wave as
+//     well as across the two waves of a SIMD.  The lazy rescale (offset moves
+//     only when a row max grows by 2^8) also rescales the pending P(t-1).
+//     The loop is unrolled by two so score and P registers trade roles
+//     instead of being copied; MFMAs are built in their VGPR form so the
+//     scores feed the vector ALUs without accumulator-register moves.
+//   * Loads never branch: keys at or past the unit's last visible key re-read
+//     that key (finite; its score is masked, its P is exactly 0), so dead page
+//     slots and table entries past the last page never reach a product.
 //   * Schedule: a persistent grid, one 8-wave workgroup per CU.  Each XCD
 //     (workgroup id mod 8) owns whole kv heads; its workgroups first run whole
 //     units in rounds, all in lockstep along the keys, so every K/V tile of a
@@ -42,6 +50,8 @@
 //     invalidate the XCD's whole L2, evicting the K/V tiles every other
 //     workgroup there is streaming.)  Without a workspace the leftover units
 //     simply run whole.
+#include <type_traits>
+
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -51,20 +61,66 @@ namespace {
 
 constexpr int kKT = 64;            // keys per tile
 constexpr int kQT = 128;           // query rows per unit
-constexpr int kThreads = 512;      // 8 waves
+constexpr int kThreads = 512;      // 8 waves, two per SIMD
 constexpr int kTableCache = 1024;  // page ids cached in LDS
 constexpr int kSlotFloats = 4 * 65 * 64;   // partial state: [row block][64 outputs + lse][lane]
 
 template <int D>
 struct PSmem {
-  static constexpr int KROW = D * 2 + 16;   // odd multiple of 16 B: conflict-free 16-B row reads
-  static constexpr int VROW = D * 2 + 64;   // 64 mod 256 B: the 4 rows x 2 dim halves of a transpose read hit distinct banks
-  static constexpr int KB = kKT * KROW;
-  static constexpr int VB = kKT * VROW;
-  static constexpr int STAGES = 2 * KB + 2 * VB;
-  static constexpr int COMBINE = 4 * 66 * 64 * 4;   // [row block][64 + 2 values][lane] floats
+  static constexpr int ROWB = D * 2;              // bytes of one key row in LDS (no padding: XOR swizzle)
+  static constexpr int CH = D / 8;                // 16-byte chunks per row
+  static constexpr int TB = kKT * ROWB;           // bytes of one K or V tile
+  static constexpr int NST = 3;                   // pipeline stages of each of K and V
+  static constexpr int STAGES = 2 * NST * TB;    // K stages, then V stages
+  static constexpr int RPI = 1024 / ROWB;         // rows written by one LDS-DMA instruction (64 lanes x 16 B)
+  static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
+  static_assert(RPI * IPW == 8, "a wave writes 8 rows of each tile");
+  static constexpr int COMBINE = 4 * 66 * 64 * 4;   // key-half join: [row block][64 + 2 values][lane] floats
   static constexpr int BYTES = STAGES > COMBINE ? STAGES : COMBINE;
 };
+
+// Chunk positions in LDS: chunk c of tile row r lives at position c ^ swz(r).
+// K: the 16 rows of one 16-lane group of a 32x32x16 operand read land on 16
+// distinct 16-byte bank slots.  V: the 4 rows x 32 bytes of one 16-lane group
+// of a transposed read (and the two dim halves of a wave) land on distinct
+// bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 2 * ((r >> 1) & 1); }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// One LDS-DMA instruction (buffer_load_dwordx4 ... lds): every lane copies 16
+// bytes at byte offset voff of the buffer [base, base + nbytes) to LDS address
+// dst + 16 * lane (base, nbytes and dst uniform); lanes outside the range write
+// zeros.  Issued from asm so that the compiler's own wait counting does not
+// see it: it would otherwise wait for every pending LDS-DMA before each LDS
+// read it cannot prove disjoint (all of them here, the stages being a ring).
+// Completion is waited for explicitly with wait_dma_and_barrier; extra
+// operations in flight can only make the compiler's own vmcnt waits longer.
+// No other code of this kernel uses M0.
+__device__ __forceinline__ void dma16(const uint8_t* base, int nbytes, uint8_t* dst, int voff) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  d[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  d[3] = 0x00020000;
+  const int m0v = __builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(dst));
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "s"(m0v), "s"(d)
+               : "memory");
+}
+
+// Wait until at most N of this wave's vector memory operations (here: LDS-DMA
+// loads) are outstanding, then join the workgroup.  Written as one asm block
+// with a memory clobber so that no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ int visible_keys(int i, int n_ctx, int seq, int cbs) {
   if (i >= seq) return 0;
@@ -185,7 +241,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   using S = PSmem<D>;
   constexpr int KSTEPS = D / 16;   // k-steps of QK^T
   constexpr int DB = D / 32;       // 32-dim output blocks
-  constexpr int LPR = D / 32;      // 16-byte loads per staging thread (a quarter of a row)
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::BYTES];
   __shared__ int32_t pages[kTableCache];
   __shared__ int32_t tcum[kMaxTailUnits + 1];
@@ -194,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int ln = lane & 31, hf = lane >> 5;
-  const int rb = wave & 3, kh = wave >> 2;
+  const int rb = wave & 3, kh = wave >> 2;   // row block, key half
   const float c = p.scale_log2;
 
   // ---- schedule: XCD xcd owns kv units xcd, xcd + 8, ...; its Gx workgroups
@@ -205,19 +260,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
   const int shift = p.page_shift;
   const int pmask = (1 << shift) - 1;
-  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
-  uint8_t* kbuf0 = smem;
-  uint8_t* vbuf0 = smem + 2 * S::KB;
-  // staging role: waves 0-3 stage K rows, waves 4-7 V rows; 4 threads per row
-  const bool stage_k = tid < 256;
-  const int srow = (tid & 255) >> 2;   // key row within a tile
-  const int squart = tid & 3;          // quarter of the row (D/4 dims)
+  const int row_b = p.num_kv_heads * D * 2;            // bytes between key rows of a page
+  const int64_t page_stride_b = p.page_stride * 2;
+  const uint8_t* kpool_b = reinterpret_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* vpool_b = reinterpret_cast<const uint8_t*>(p.v_pool);
 
-
-  // one segment: tiles [t0, t1) of unit u (ut tiles in all).  F and C place
-  // the segment in the XCD's stream-K order when it is a piece of a split unit.
+  // one segment: tiles [t0, t1) of unit u (ut tiles in all); first_seg tells
+  // which of the workgroup's two slots a partial state goes to.
   auto run = [&](int u, int t0, int t1, int ut, bool first_seg) {
     const Unit x = unit_of(p, u);
     const int32_t* trow = p.table + (int64_t)x.b * p.table_stride;
@@ -233,13 +282,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       const uint16_t* qp =
           p.q + ((int64_t)x.b * p.s_q + (ok ? my_row : 0)) * p.q_tok_stride + (int64_t)x.h * p.q_head_stride;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) q[s] = ok ? ld16(qp + 16 * s + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
+      for (int s2 = 0; s2 < KSTEPS; ++s2) q[s2] = ok ? ld16(qp + 16 * s2 + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
     }
 
     f32x16 o[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{};
-    float mc = kNegInf, l = 0.f;   // exponent offset (log2 units) and running sum of this wave
+    float mc = kNegInf, l = 0.f;   // exponent offset (log2 units) and this lane's share of the row sum
 
     if (t1 > t0) {
       // page ids of the walked keys, refreshed if the segment spans more pages
@@ -253,122 +302,189 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       };
       cache_pages(page_base);
 
-      // staging: this thread's 16-byte pieces of one key row (K or V) of tile t
-      u32x4 st[LPR];
-      auto fetch = [&](int t) {
-        int key = t * kKT + srow;
-        key = key < x.kmax ? key : x.kmax - 1;   // clamp: always a valid row; replaced by zeros below
-        const int pg = pages[(key >> shift) - page_base];
-        const uint16_t* src = (stage_k ? kpool : vpool) + (int64_t)pg * p.page_stride +
-                              (int64_t)(key & pmask) * row_elems + (int64_t)x.g * D;
-        // K: a contiguous quarter row per thread; V: 16-byte pieces squart, squart + 4, ...
-        // (each layout keeps 16 consecutive lanes on distinct LDS banks when stored)
+      // LDS-DMA of tile t of K or V into its stage: this wave writes rows
+      // 8 wave .. 8 wave + 7 (one page: page_size >= 16).  Keys past the unit's
+      // last visible key re-read that key (a finite row: its score is masked
+      // and its P is 0); tiles past the segment issue zero-range loads that
+      // only write zeros into a free stage, so every iteration has the same
+      // loads in flight.
+      const int64_t head_off_b = (int64_t)x.g * D * 2;
+      const int rec_bytes = ((1 << shift) - 1) * row_b + D * 2;
+      auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::TB; };
+      auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::TB; };
+      auto dma_tile = [&](const uint8_t* pool_b, uint8_t* tile, int t, bool is_k) {
+        const bool live = t < t1;
+        const int kmax1 = x.kmax - 1;
+        int pg = 0;
+        if (live) pg = __builtin_amdgcn_readfirstlane(pages[(min(t * kKT + 8 * wave, kmax1) >> shift) - page_base]);
+        const uint8_t* base = pool_b + (int64_t)pg * page_stride_b + head_off_b;
 #pragma unroll
-        for (int e = 0; e < LPR; ++e) st[e] = ld16(src + (stage_k ? (D / 4) * squart + 8 * e : 8 * (squart + 4 * e)));
-      };
-      auto commit = [&](int t, bool want_k, bool want_v) {
-        const bool live = t * kKT + srow < x.kmax;
-        if (stage_k ? want_k : want_v) {
-          uint8_t* dst = stage_k ? kbuf0 + (t & 1) * S::KB + srow * S::KROW + (D / 2) * squart
-                                 : vbuf0 + (t & 1) * S::VB + srow * S::VROW + 16 * squart;
-#pragma unroll
-          for (int e = 0; e < LPR; ++e)
-            *reinterpret_cast<u32x4*>(dst + (stage_k ? 16 * e : 64 * e)) = live ? st[e] : u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < S::IPW; ++j) {
+          const int r0 = S::RPI * (wave * S::IPW + j);
+          const int r = r0 + lane / S::CH;
+          const int key = min(t * kKT + r, kmax1);
+          const int cc = (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
+          dma16(base, live ? rec_bytes : 0, tile + r0 * S::ROWB, (key & pmask) * row_b + cc * 16);
         }
       };
-      // S^T for this wave's key half of tile t (K buffer t & 1)
-      auto qk = [&](int t) {
-        f32x16 acc = f32x16{};
-        const uint8_t* krow = kbuf0 + (t & 1) * S::KB + (32 * kh + ln) * S::KROW + 16 * hf;
+      // S^T of this wave's key half of K tile t: keys 32 kh + 8 (i / 4) + 4 hf + (i % 4)
+      auto qk = [&](int t, f32x16& acc) {
+        const uint8_t* kt = kstage(t);
+        const int kr = 32 * kh + ln;
+        u32x4 a[KSTEPS];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          acc = mfma32x32x16_bf16(*reinterpret_cast<const u32x4*>(krow + 32 * s), q[s], acc);
-        return acc;
+        for (int s2 = 0; s2 < KSTEPS; ++s2)
+          a[s2] = *reinterpret_cast<const u32x4*>(kt + kr * S::ROWB + (((2 * s2 + hf) ^ swz_k<D>(kr)) << 4));
+        acc = f32x16{};
+#pragma unroll
+        for (int s2 = 0; s2 < KSTEPS; ++s2) acc = mfma32x32x16_bf16(a[s2], q[s2], acc);
+      };
+      // O^T += V^T P^T over this wave's key half of V tile t; pk[mu] is the bf16
+      // P of keys 32 kh + 16 mu + 8 (j / 4) + 4 hf + (j % 4), j = 0..7.  Lane
+      // group (hf, dh) reads rows 32 kh + 16 mu + 4 hf + 0..3 (and + 8) of dims
+      // 32 d + 16 dh .. + 15, transposed.
+      auto pv = [&](int t, const u32x4 (&pk)[2]) {
+        const uint8_t* vt = vstage(t);
+        const int s16 = lane & 15;
+        const int dh = (lane >> 4) & 1;
+        u32x2 lo[2][DB], hi[2][DB];
+#pragma unroll
+        for (int mu = 0; mu < 2; ++mu) {
+          const int r = 32 * kh + 16 * mu + 4 * hf + (s16 >> 2);
+          const uint8_t* rowp = vt + r * S::ROWB + 8 * (s16 & 1);
+          const int sw = swz_v<D>(r);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            const uint8_t* a0 = rowp + (((4 * d + 2 * dh + ((s16 & 3) >> 1)) ^ sw) << 4);
+            lo[mu][d] = lds_read_tr(a0);
+            hi[mu][d] = lds_read_tr(a0 + 8 * S::ROWB);
+          }
+        }
+#pragma unroll
+        for (int mu = 0; mu < 2; ++mu)
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+            o[d] = mfma32x32x16_bf16(u32x4{lo[mu][d][0], lo[mu][d][1], hi[mu][d][0], hi[mu][d][1]}, pk[mu], o[d]);
+      };
+      // row max of this wave's 32 scores of tile t, masking keys at or past
+      // the row's limit when the half reaches past the wave's smallest limit
+      auto mask_max = [&](f32x16& sv, int t, auto masked) {
+        if constexpr (decltype(masked)::value) {
+          const int key0 = t * kKT + 32 * kh;
+          if (key0 + 32 > wmin) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= my_lim) sv[i] = kNegInf;
+          }
+        }
+        float m0 = fmaxf(sv[0], sv[1]), m1 = fmaxf(sv[2], sv[3]);
+#pragma unroll
+        for (int i = 4; i < 16; i += 2) {
+          m0 = fmaxf(m0, sv[i]);
+          m1 = fmaxf(m1, sv[i + 1]);
+        }
+        const float m = fmaxf(m0, m1);
+        // lanes l and l ^ 32 hold the same query row
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       };
 
-      // prologue: K(t0), V(t0) -> LDS; S(t0); K(t0+1) -> LDS
+      // prologue: zeros into V(t0-1)'s stage (the first PV uses it with P = 0);
+      // K(t0), K(t0+1), V(t0) landed; K(t0+2) in flight; S(t0); a barrier
+      // before K(t0)'s stage is refilled with K(t0+3)
       const bool need_refresh = ((t1 * kKT - 1) >> shift) - page_base >= kTableCache;
-      fetch(t0);
-      commit(t0, true, true);
-      __syncthreads();
-      f32x16 sc = qk(t0);
-      if (t0 + 1 < t1) {
-        fetch(t0 + 1);
-        commit(t0 + 1, true, false);
-      }
+      dma_tile(vpool_b, vstage(t0 - 1), t1, false);
+      dma_tile(kpool_b, kstage(t0), t0, true);
+      dma_tile(kpool_b, kstage(t0 + 1), t0 + 1, true);
+      dma_tile(vpool_b, vstage(t0), t0, false);
+      dma_tile(kpool_b, kstage(t0 + 2), t0 + 2, true);
+      wait_dma_and_barrier<S::IPW>();
+      f32x16 sA, sB;
+      u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+      qk(t0, sA);
+      float mt = mask_max(sA, t0, std::true_type{});
       __syncthreads();
 
-      for (int t = t0; t < t1; ++t) {
-        // invariant: LDS holds K(t+1) (if any) and V(t); sc = S^T(t)
-        const bool more_k = t + 2 < t1, more_v = t + 1 < t1;
-        if (need_refresh && more_v) {
-          const int want = (((more_k ? t + 2 : t + 1) * kKT + kKT - 1) >> shift) - page_base;
-          if (want >= kTableCache) cache_pages(((t + 1) * kKT) >> shift);
+      // iteration t: exp of S(t) -> P(t); QK^T of tile t+1 (zeros past the
+      // segment); PV of tile t-1 (P = 0 before the first); max of S(t+1).
+      // s_cur / p_cur and s_next / p_prev trade roles between iterations.
+      auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked) {
+        // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight
+        if (need_refresh) {
+          const int last_t = t + 3 < t1 ? t + 3 : t1 - 1;
+          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) cache_pages(((t + 1) * kKT) >> shift);
         }
-        // global loads of the next stage: K(t+2) or V(t+1), by role
-        if (stage_k ? more_k : more_v) fetch(stage_k ? t + 2 : t + 1);
-        // QK^T of tile t+1 (its MFMAs overlap the softmax below)
-        f32x16 sn = f32x16{};
-        if (more_v) sn = qk(t + 1);
-        // ---- softmax of tile t (this wave's 32 keys, row = lane & 31)
-        const int key0 = t * kKT + 32 * kh;
-        if (key0 + 32 > wmin) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (key0 + 8 * (i >> 2) + 4 * hf + (i & 3) >= my_lim) sc[i] = kNegInf;
-        }
-        float mt = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        // refill: K(t+3) into K(t)'s stage, V(t+1) into V(t-2)'s stage
+        dma_tile(kpool_b, kstage(t + 3), t + 3, true);
+        dma_tile(vpool_b, vstage(t + 1), t + 1, false);
+        // lazy rescale: the offset of a row moves only when its max grows by
+        // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
         const float mtc = mt * c;
-        const bool grow = mtc > mc + 8.0f;   // lazy rescale: the offset moves only by > 2^8
+        const bool grow = mtc > mc + 8.0f;
         if (__any(grow)) {
           const float mc_new = grow ? mtc : mc;
           const float alpha = (mc == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
           l *= alpha;
 #pragma unroll
           for (int d = 0; d < DB; ++d) o[d] *= alpha;
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t v = p_prev[k][w];
+              p_prev[k][w] = pack_bf16x2(__uint_as_float(v << 16) * alpha, __uint_as_float(v & 0xffff0000u) * alpha);
+            }
           mc = mc_new;
         }
         const float mcu = (mc == kNegInf) ? 0.f : mc;
-        u32x4 pb[2];
         float psum = 0.f;
 #pragma unroll
         for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            const float e0 = fast_exp2(fmaf(sc[8 * mu + 2 * q2], c, -mcu));
-            const float e1 = fast_exp2(fmaf(sc[8 * mu + 2 * q2 + 1], c, -mcu));
+            const float e0 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2], c, -mcu));
+            const float e1 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2 + 1], c, -mcu));
             psum += e0 + e1;
-            pb[mu][q2] = pack_bf16x2(e0, e1);
+            p_cur[mu][q2] = pack_bf16x2(e0, e1);
           }
         l += psum;
-        // ---- O^T += V^T P^T: V^T operands by transposed LDS reads
-        {
-          const uint8_t* vb = vbuf0 + (t & 1) * S::VB;
-          const int s16 = lane & 15;
-          const int dh = (lane >> 4) & 1;
-#pragma unroll
-          for (int mu = 0; mu < 2; ++mu) {
-            const int kb = 32 * kh + 16 * mu + 4 * hf + (s16 >> 2);
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-              const uint8_t* a0 = vb + kb * S::VROW + (32 * d + 16 * dh + 4 * (s16 & 3)) * 2;
-              const u32x2 lo = lds_read_tr(a0);
-              const u32x2 hi = lds_read_tr(a0 + 8 * S::VROW);
-              o[d] = mfma32x32x16_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[mu], o[d]);
-            }
-          }
-        }
-        commit(stage_k ? t + 2 : t + 1, more_k, more_v);
-        __syncthreads();
-        sc = sn;
+        qk(t + 1, s_next);
+        pv(t - 1, p_prev);
+        mt = mask_max(s_next, t + 1, masked);
+        // K(t+2) and V(t) have landed once only this iteration's loads remain
+        wait_dma_and_barrier<2 * S::IPW>();
+      };
+      // iteration t masks tile t+1: this wave's keys up to 64 t + 96 + 32 kh - 1.
+      // It needs no mask when they lie wholly below every row's key limit.
+      // (Waves may switch loops at different t: every step has one barrier.)
+      const int off = 96 + 32 * kh;
+      int t_mask = wmin < off ? t0 : (wmin - off) / kKT + 1;   // first t with 64 t + off > wmin
+      t_mask = t_mask < t0 ? t0 : (t_mask > t1 ? t1 : t_mask);
+      int t = t0;
+      for (; t + 1 < t_mask; t += 2) {
+        step(t, sA, sB, pA, pB, std::false_type{});
+        step(t + 1, sB, sA, pB, pA, std::false_type{});
       }
+      for (; t + 1 < t1; t += 2) {
+        step(t, sA, sB, pA, pB, std::true_type{});
+        step(t + 1, sB, sA, pB, pA, std::true_type{});
+      }
+      if (t < t1) {
+        step(t, sA, sB, pA, pB, std::true_type{});
+        pB[0] = pA[0];
+        pB[1] = pA[1];
+      }
+      // PV of the last tile (its P is in pB), then drain the trailing
+      // zero-range loads before the stages are reused
+      pv(t1 - 1, pB);
+      wait_dma_and_barrier<0>();
     }
 
     // ---- join the two key halves of each row block through LDS
-    l += __shfl_xor(l, 32, 64);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+      l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     __syncthreads();
     float* cmb = reinterpret_cast<float*>(smem) + rb * 66 * 64;   // [66][64] floats per row block
     if (kh == 1) {

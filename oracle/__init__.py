@@ -12,11 +12,13 @@ from .pkv_oracle import (  # noqa: F401
     attention_rows,
     attn_decode,
     attn_prefill_block_causal,
+    copy_slots,
     decode_bf16,
     decode_e4m3fn,
     e4m3fn_table,
     gather_logical,
     merge_states,
     prefill_visible_keys,
+    rotate_rows,
     scatter_slots,
 )

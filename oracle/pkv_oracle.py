@@ -326,3 +326,52 @@ def merge_states(o_parts: np.ndarray, lse_parts: np.ndarray):
     o = np.where(empty[..., None], 0.0, o)
     lse = np.where(empty, -np.inf, m_safe + np.log(w_sum_safe))
     return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Exact-window commit operations  [P1] Description / Cache (eviction is an
+# in-place rotation of the page table; commit fills the private pages with one
+# pool-to-pool copy whose table carries sentinel entries)
+# ----------------------------------------------------------------------------
+
+def rotate_rows(rows: np.ndarray, shift: int) -> np.ndarray:
+    """In-place rotation of every row of a 2-D array, returned as a new array.
+
+    Element ``c`` of a row takes the old element ``(c + shift) mod cols``: the
+    first ``shift`` entries (the oldest window pages) move to the end of the
+    row.  Any integer shift is allowed (negative or larger than the row); rows
+    of at most one element and empty arrays are unchanged.
+    """
+    rows = np.asarray(rows)
+    out = rows.copy()
+    n_rows, cols = rows.shape
+    if n_rows == 0 or cols <= 1:
+        return out
+    s = shift % cols
+    for r in range(n_rows):
+        for c in range(cols):
+            out[r, c] = rows[r, (c + s) % cols]
+    return out
+
+
+def copy_slots(pool: np.ndarray, src_slots, dst_slots) -> np.ndarray:
+    """Pool-to-pool copy of whole key rows, returned as a new pool.
+
+    ``pool`` is ``[layers, num_pages, page_size, H, D]`` raw storage (one of K
+    or V).  Entry i copies slot ``src_slots[i]`` to slot ``dst_slots[i]`` in
+    every layer (slot = page * page_size + row, all heads, all dims).  An
+    entry with a negative source or destination is a sentinel and is skipped.
+    Entries are applied in order, reading the pool as it was before the call
+    (a destination that is another entry's source is not defined by the op;
+    callers keep them disjoint).
+    """
+    pool = np.asarray(pool)
+    out = pool.copy()
+    layers, n_pages, page_size = pool.shape[:3]
+    flat_in = pool.reshape(layers, n_pages * page_size, *pool.shape[3:])
+    flat_out = out.reshape(layers, n_pages * page_size, *pool.shape[3:])
+    for s, d in zip(np.asarray(src_slots).tolist(), np.asarray(dst_slots).tolist()):
+        if s < 0 or d < 0:
+            continue
+        flat_out[:, d] = flat_in[:, s]
+    return out

@@ -402,3 +402,47 @@ def test_prefix_tail_merge_equals_full_attention_through_tables():
     o_full, lse_full = orc.attn_decode(kp, vp, q, full, [prefix_len + t for t in tails], 0.3, "f32")
     np.testing.assert_allclose(o, o_full, atol=1e-13)
     np.testing.assert_allclose(lse, lse_full, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- exact-window commit ops
+
+
+def test_rotate_rows_hand_worked_fixture():
+    for line in open(os.path.join(GOLDEN, "rotate_rows.txt")).read().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        shift, before, after = (part.strip() for part in line.split("|"))
+        row = np.array([[int(v) for v in before.split()]])
+        assert orc.rotate_rows(row, int(shift)).tolist() == [[int(v) for v in after.split()]]
+
+
+@pytest.mark.parametrize("shape", [(1, 5), (3, 8), (7, 33), (2, 1), (3, 0), (0, 4)])
+@pytest.mark.parametrize("shift", [0, 1, 3, -2, 64, -1000003])
+def test_rotate_rows_matches_numpy_roll(shape, shift):
+    rng = np.random.default_rng(abs(shift) + shape[1])
+    x = rng.integers(-(2 ** 31), 2 ** 31, size=shape, dtype=np.int64).astype(np.int32)
+    expect = np.roll(x, -shift, axis=1) if shape[1] > 0 else x
+    assert np.array_equal(orc.rotate_rows(x, shift), expect)
+
+
+def test_rotate_rows_composes_and_inverts():
+    x = np.arange(6 * 11, dtype=np.int32).reshape(6, 11)
+    assert np.array_equal(orc.rotate_rows(orc.rotate_rows(x, 4), 9), orc.rotate_rows(x, 13))
+    assert np.array_equal(orc.rotate_rows(orc.rotate_rows(x, 5), -5), x)
+    assert np.array_equal(orc.rotate_rows(x, 11), x)
+
+
+def test_copy_slots_matches_fancy_indexing_and_skips_sentinels():
+    rng = np.random.default_rng(5)
+    layers, pages, ps, h, d = 3, 12, 4, 2, 8
+    pool = rng.integers(0, 65536, size=(layers, pages, ps, h, d), dtype=np.int64).astype(np.uint16)
+    src = np.array([3, 7, -1, 20, 44, 5], dtype=np.int64)
+    dst = np.array([30, 31, 9, -4, 2, 47], dtype=np.int64)
+    got = orc.copy_slots(pool, src, dst)
+    flat = pool.reshape(layers, pages * ps, h, d).copy()
+    keep = (src >= 0) & (dst >= 0)
+    flat[:, dst[keep]] = pool.reshape(layers, pages * ps, h, d)[:, src[keep]]
+    assert np.array_equal(got, flat.reshape(pool.shape))
+    # sentinel destinations and untouched slots keep their bytes
+    untouched = np.setdiff1d(np.arange(pages * ps), dst[keep])
+    assert np.array_equal(got.reshape(layers, -1, h, d)[:, untouched], pool.reshape(layers, -1, h, d)[:, untouched])

@@ -1,6 +1,6 @@
 """Benchmark of the paged K/V-cache path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,shared,fp8] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,shared,fp8,commit] [--no-cpu-baseline]
 
 Prints ONE JSON line.  The headline workload is the bf16 GQA decode (64
 sequences, lengths uniform in [512, 4096], 32 q / 8 kv heads of 128, 32-token
@@ -52,8 +52,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", default="prefill,shared,fp8",
-                    help="secondary workloads to run: comma list of prefill, shared, fp8 (or none)")
+    ap.add_argument("--workloads", default="prefill,shared,fp8,commit",
+                    help="secondary workloads to run: comma list of prefill, shared, fp8, commit (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -313,6 +313,43 @@ def run_long_fp8(torch, pkv, W, flush):
             "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def run_commit(torch, pkv, W, flush):
+    """Exact-window commit ops at the block-causal prefill's geometry (24 kv
+    heads x 128, bf16, 32-token pages, 512-page pool): a private-page fill of
+    2048 slots in each of 8 layers, and the rotation of the page-table row."""
+    layers, pages, ps, hkv, d = 8, 512, 32, 24, 128
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(7)
+    k = torch.randn((layers, pages, ps, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    v = torch.randn((layers, pages, ps, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    pool = pkv.Pool(k[0], v[0])
+    perm = torch.randperm(pages * ps, generator=torch.Generator().manual_seed(8))
+    src = perm[:2048].to("cuda:0", torch.int64)
+    dst = perm[2048:4096].to("cuda:0", torch.int64)
+    layer_stride = pages * ps * hkv * d
+
+    def copy():
+        pkv.pkv_copy_slots(pool, src, dst, layers, layer_stride)
+
+    for _ in range(3):
+        copy()
+    med, p10, p90 = time_events(torch, copy, 30, flush)
+    nbytes = 2 * 2 * 2048 * layers * hkv * d * 2 + 2 * 2048 * 8     # K and V rows read + written, slot ids
+    table = torch.arange(209, dtype=torch.int32, device="cuda:0")
+
+    def rot():
+        pkv.pkv_rotate_rows(table, 32)
+
+    for _ in range(3):
+        rot()
+    rmed, _, _ = time_events(torch, rot, 30, flush)
+    return {"workload": "exact-window commit: private-page fill of 2048 slots x 8 layers (24 kv heads x 128, bf16, "
+                        "32-token pages) and the rotation of a 209-page table row",
+            "copy_slots_mb": nbytes / 1e6, "copy_slots_ms": med, "copy_slots_ms_p10_p90": [p10, p90],
+            "copy_slots_gbs": nbytes / (med * 1e-3) / 1e9, "copy_slots_frac_hbm_peak": nbytes / (med * 1e-3) / 1e9 /
+            HBM_PEAK_GBS, "rotate_rows_ms": rmed}
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(case, seconds):
@@ -396,7 +433,7 @@ def main():
     workloads = {}
     flush = Flusher(torch)
     runners = {"prefill": ("block_causal_prefill", run_prefill), "shared": ("shared_prefix_decode", run_shared_prefix),
-               "fp8": ("long_fp8_decode", run_long_fp8)}
+               "fp8": ("long_fp8_decode", run_long_fp8), "commit": ("exact_window_commit", run_commit)}
     for name in [w.strip() for w in args.workloads.split(",") if w.strip() and w.strip() != "none"]:
         key, fn = runners[name]
         workloads[key] = fn(torch, pkv, W, flush)

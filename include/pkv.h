@@ -235,6 +235,49 @@ pkv_status pkv_merge_states(const float* o_parts, const float* lse_parts, int32_
                             int32_t num_q_heads, int32_t head_dim, void* out, pkv_dtype out_dtype,
                             float* out_lse, hipStream_t stream);
 
+/*
+ * pkv_rotate_rows -- in-place rotation of the rows of a 2-D array (page-table
+ * eviction).
+ * [P1] Description / Cache (eviction from the rolling history window is an
+ * in-place rotation of the page table on the device, not a reallocation).
+ *
+ *   data        device pointer to element (0, 0); element (r, c) is at byte
+ *               (r * row_stride + c) * elem_size.  Rotated in place.
+ *   rows, cols  >= 0.  row_stride >= cols (elements).
+ *   elem_size   1, 2, 4, 8 or 16 bytes.
+ *   shift       any integer: element c takes the old element
+ *               (c + shift) mod cols (the first shift entries move to the
+ *               end of the row).
+ * rows == 0, cols <= 1 or shift == 0 mod cols: no launch (data may be NULL).
+ * Errors: PKV_ERR_NULL (data NULL with work to do); PKV_ERR_SHAPE (negative
+ * sizes, row_stride < cols); PKV_ERR_UNSUPPORTED (elem_size); PKV_ERR_ALIGN
+ * (data not aligned to elem_size); PKV_ERR_HIP.
+ */
+pkv_status pkv_rotate_rows(void* data, int64_t rows, int64_t cols, int64_t row_stride, int32_t elem_size,
+                           int64_t shift, hipStream_t stream);
+
+/*
+ * pkv_copy_slots -- pool-to-pool copy of key rows (private-page fill).
+ * [P1] Description / Cache (commit fills the causal blocks' private pages
+ * with one pool-to-pool copy; the copy's entry list carries sentinels).
+ *
+ *   pool          as for pkv_scatter_slots; layer l of a multi-layer pool
+ *                 starts at k + l * layer_stride (and v + l * layer_stride).
+ *   num_layers    >= 1; layer_stride (elements) >= num_pages * page_stride
+ *                 when num_layers > 1.
+ *   src_slots,    device int64 [n]: entry i copies slot src_slots[i] to slot
+ *   dst_slots     dst_slots[i] (whole key row: every kv head and dim, K and
+ *                 V) in every layer.  A negative source or destination is a
+ *                 sentinel: the entry is skipped.  Destinations must be
+ *                 distinct and no destination may be another entry's source
+ *                 (otherwise the result is not defined).  Slots must lie in
+ *                 the pool.  fp8 scales are not touched.
+ * n == 0: no launch.
+ * Errors: as pkv_scatter_slots; bad num_layers / layer_stride -> PKV_ERR_SHAPE.
+ */
+pkv_status pkv_copy_slots(const pkv_pool* pool, int32_t num_layers, int64_t layer_stride, const int64_t* src_slots,
+                          const int64_t* dst_slots, int64_t n, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

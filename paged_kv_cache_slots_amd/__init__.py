@@ -29,7 +29,7 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
 
 EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
             "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
-            "pkv_merge_states"]
+            "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots"]
 
 
 class PkvError(RuntimeError):
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
                                                          P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
+        "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
+        "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -199,3 +201,31 @@ def pkv_merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.
     _check("pkv_merge_states", load_library().pkv_merge_states(
         o_parts.data_ptr(), lse_parts.data_ptr(), n, r, hq, d, out.data_ptr(), _dtype_code(out.dtype),
         _ptr(out_lse), _stream(stream)))
+
+
+def pkv_rotate_rows(rows: torch.Tensor, shift: int, stream=None) -> None:
+    """Rotate every row of ``rows`` in place: element c takes the old element
+    (c + shift) mod cols.  ``rows`` is 1-D (one row) or 2-D with contiguous
+    elements inside a row (any row stride); element size 1, 2, 4, 8 or 16."""
+    t = rows if rows.dim() == 2 else rows.view(1, -1)
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("rows must be 1-D or 2-D with contiguous elements within a row")
+    n_rows, cols = t.shape
+    row_stride = t.stride(0) if n_rows > 1 else cols
+    _check("pkv_rotate_rows", load_library().pkv_rotate_rows(
+        t.data_ptr() if t.numel() else None, n_rows, cols, row_stride, t.element_size(), int(shift),
+        _stream(stream)))
+
+
+def pkv_copy_slots(pool: Pool, src_slots: torch.Tensor, dst_slots: torch.Tensor, num_layers: int = 1,
+                   layer_stride: int = 0, stream=None) -> None:
+    """Copy whole key rows (every kv head, K and V) from int64 slots
+    ``src_slots`` to ``dst_slots`` in each of ``num_layers`` layers of the
+    pool (layer l starts ``layer_stride`` elements after layer l-1); entries
+    with a negative slot are skipped."""
+    if src_slots.numel() != dst_slots.numel():
+        raise ValueError("src_slots and dst_slots must have the same length")
+    ps = pool.struct()
+    _check("pkv_copy_slots", load_library().pkv_copy_slots(
+        ctypes.byref(ps), num_layers, layer_stride, src_slots.data_ptr(), dst_slots.data_ptr(), src_slots.numel(),
+        _stream(stream)))

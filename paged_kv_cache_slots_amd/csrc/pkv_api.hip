@@ -353,4 +353,58 @@ pkv_status pkv_merge_states(const float* o_parts, const float* lse_parts, int32_
   return launch_merge(m, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_rotate_rows(void* data, int64_t rows, int64_t cols, int64_t row_stride, int32_t elem_size,
+                           int64_t shift, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || row_stride < cols) return PKV_ERR_SHAPE;
+  if (elem_size != 1 && elem_size != 2 && elem_size != 4 && elem_size != 8 && elem_size != 16)
+    return PKV_ERR_UNSUPPORTED;
+  if (rows == 0 || cols <= 1) return PKV_OK;   // nothing moves; empty tensors may carry NULL pointers
+  const int64_t s = ((shift % cols) + cols) % cols;
+  if (s == 0) return PKV_OK;
+  if (!data) return PKV_ERR_NULL;
+  if (!aligned(data, elem_size)) return PKV_ERR_ALIGN;
+  RotateParams p;
+  p.data = static_cast<uint8_t*>(data);
+  p.rows = rows;
+  p.cols = cols;
+  p.row_stride_b = row_stride * elem_size;
+  p.shift = s;
+  return launch_rotate(p, elem_size, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_copy_slots(const pkv_pool* pool, int32_t num_layers, int64_t layer_stride, const int64_t* src_slots,
+                          const int64_t* dst_slots, int64_t n, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (n < 0 || num_layers < 1 || layer_stride < 0) return PKV_ERR_SHAPE;
+  if (num_layers > 1 && layer_stride < pool->num_pages * pool->page_stride) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!src_slots || !dst_slots) return PKV_ERR_NULL;
+  const int es = elem_bytes(pool->dtype);
+  const int64_t row_b = (int64_t)pool->num_kv_heads * pool->head_dim * es;
+  int vec = 16;
+  while (vec > 1) {
+    const bool ok = row_b % vec == 0 && aligned(pool->k, vec) && aligned(pool->v, vec) &&
+                    (pool->page_stride * es) % vec == 0 && (layer_stride * es) % vec == 0;
+    if (ok) break;
+    vec >>= 1;
+  }
+  CopySlotsParams p;
+  p.pool_k = static_cast<uint8_t*>(pool->k);
+  p.pool_v = static_cast<uint8_t*>(pool->v);
+  p.src = src_slots;
+  p.dst = dst_slots;
+  p.n = n;
+  p.layer_stride_b = layer_stride * es;
+  p.page_stride_b = pool->page_stride * es;
+  p.row_b = row_b;
+  p.page_shift = log2i(pool->page_size);
+  p.num_layers = num_layers;
+  p.vecs_per_row = (int32_t)(row_b / vec);
+  return launch_copy_slots(p, vec, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // extern "C"

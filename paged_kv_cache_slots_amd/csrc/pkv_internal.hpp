@@ -111,6 +111,30 @@ struct PrefillParams {
   float scale_log2;
 };
 
+// In-place rotation of rows: element c takes the old element (c + shift) mod cols.
+struct RotateParams {
+  uint8_t* data;
+  int64_t rows;
+  int64_t cols;
+  int64_t row_stride_b;       // bytes between rows
+  int64_t shift;              // normalised to 1 .. cols - 1
+};
+
+// Pool-to-pool copy of whole key rows (all heads, K and V) in every layer.
+struct CopySlotsParams {
+  uint8_t* pool_k;
+  uint8_t* pool_v;
+  const int64_t* src;
+  const int64_t* dst;
+  int64_t n;
+  int64_t layer_stride_b;     // bytes between layers
+  int64_t page_stride_b;      // bytes between pages
+  int64_t row_b;              // bytes of one key row of a page (= Hkv * D * esize)
+  int32_t page_shift;
+  int32_t num_layers;
+  int32_t vecs_per_row;       // row_b / vec_bytes
+};
+
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);
@@ -119,6 +143,8 @@ hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, in
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
+hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);
+hipError_t launch_copy_slots(const CopySlotsParams& p, int vec_bytes, hipStream_t stream);
 int64_t prefill_units(int32_t batch, int32_t s_q, int32_t num_q_heads);
 size_t prefill_slot_bytes();
 

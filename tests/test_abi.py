@@ -123,3 +123,30 @@ def test_workspace_sizes():
     assert lib.pkv_attn_decode_workspace_bytes(256, 1, 64, 8, 128, 32768) == max(16 * 256 * 64 * 129 * 4,
                                                                                 sk(256, 128))
     assert lib.pkv_attn_decode_workspace_bytes(0, 1, 64, 8, 128, 32768) == 0
+
+
+def test_rotate_rows_argument_checks():
+    lib = pkv.load_library()
+    assert lib.pkv_rotate_rows(None, 4, 8, 8, 4, 3, None) == 1
+    assert lib.pkv_rotate_rows(A, -1, 8, 8, 4, 3, None) == 2
+    assert lib.pkv_rotate_rows(A, 4, 8, 7, 4, 3, None) == 2
+    assert lib.pkv_rotate_rows(A, 4, 8, 8, 3, 3, None) == 4
+    assert lib.pkv_rotate_rows(A + 2, 4, 8, 8, 4, 3, None) == 6
+    # nothing moves: no launch, NULL allowed
+    assert lib.pkv_rotate_rows(None, 0, 8, 8, 4, 3, None) == 0
+    assert lib.pkv_rotate_rows(None, 4, 1, 1, 4, 3, None) == 0
+    assert lib.pkv_rotate_rows(None, 4, 0, 0, 4, 3, None) == 0
+    assert lib.pkv_rotate_rows(None, 4, 8, 8, 4, 16, None) == 0
+    assert lib.pkv_rotate_rows(None, 4, 8, 8, 4, -8, None) == 0
+
+
+def test_copy_slots_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+    assert lib.pkv_copy_slots(ctypes.byref(p), 1, 0, None, A, 4, None) == 1
+    assert lib.pkv_copy_slots(ctypes.byref(p), 1, 0, A, A, -1, None) == 2
+    assert lib.pkv_copy_slots(ctypes.byref(p), 0, 0, A, A, 4, None) == 2
+    assert lib.pkv_copy_slots(ctypes.byref(p), 2, 5, A, A, 4, None) == 2
+    assert lib.pkv_copy_slots(ctypes.byref(p), 1, 0, None, None, 0, None) == 0
+    bad = _pool(page_size=48)
+    assert lib.pkv_copy_slots(ctypes.byref(bad), 1, 0, A, A, 4, None) == 2

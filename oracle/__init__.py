@@ -12,6 +12,8 @@ from .pkv_oracle import (  # noqa: F401
     attention_rows,
     attn_decode,
     attn_prefill_block_causal,
+    causal_layout,
+    causal_layout_bounds,
     copy_slots,
     decode_bf16,
     decode_e4m3fn,
@@ -21,4 +23,6 @@ from .pkv_oracle import (  # noqa: F401
     prefill_visible_keys,
     rotate_rows,
     scatter_slots,
+    visible_keys,
+    window_evicted_tokens,
 )

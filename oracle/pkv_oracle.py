@@ -375,3 +375,165 @@ def copy_slots(pool: np.ndarray, src_slots, dst_slots) -> np.ndarray:
             continue
         flat_out[:, d] = flat_in[:, s]
     return out
+
+
+# ----------------------------------------------------------------------------
+# Exact-window layout  [P1] Description / Cache (the sequence is [fixed region |
+# rolling history window | staged tokens]; a table row can start a key sequence
+# only at a page boundary, so every causal block gets private pages at the end
+# of its row holding the visible keys of the partly visible pages, then the
+# block's own tokens, which stay the last keys of the row) and the review thread
+# on the private-page regions (committed_private is copied at commit,
+# current_private every forward; bounds 3 (page_size - 1) and 2 (page_size - 1)).
+#
+# Readings (the pages give the regions, not formulas):
+# * a causal block whose first key is at logical position s sees the fixed
+#   region [0, pin), the ``window`` positions just before s, and itself;
+# * the fixed region owns ceil(pin / page_size) pages; the rolling region
+#   (positions >= pin) starts on a page of its own, so rolling position x sits
+#   at offset (x - pin) of the rolling pages, of which the first ``evicted``
+#   tokens' pages have been rotated out;
+# * the table row of the sequence is [fixed pages | rolling pages], entry
+#   F + j holding rolling page (evicted / page_size + j);
+# * a block's row is its fully visible pages (all keys visible and before the
+#   block), in logical order, then private pages that hold, packed in logical
+#   order, every other visible key before the block and then the block's own
+#   keys; a block with no such keys whose first key starts a rolling page reads
+#   its own keys from their own pages instead and needs no private copy.
+# ----------------------------------------------------------------------------
+
+def window_evicted_tokens(page_size: int, pin: int, window: int, committed: int) -> int:
+    """Rolling tokens before the first page any later block can see.
+
+    After ``committed`` tokens, the next block starts at ``committed`` and its
+    window at max(pin, committed - window); whole rolling pages before that
+    start are never read again.
+    """
+    first_needed = max(0, committed - window - pin)
+    return (first_needed // page_size) * page_size
+
+
+def visible_keys(start: int, end: int, pin: int, window: int) -> list:
+    """Logical positions a causal block [start, end) attends to, ascending."""
+    window_start = max(pin, start - window)
+    return [x for x in range(end) if x < pin or x >= window_start]
+
+
+def causal_layout_bounds(page_size: int, pin: int, window: int, block_sizes) -> dict:
+    """Sizes a geometry needs: fixed and rolling table pages, private pages per
+    block, per-block row width and piece-list capacity per block."""
+    ps = page_size
+    total = int(sum(block_sizes))
+    biggest = int(max(block_sizes)) if len(block_sizes) else 0
+    pieces = 3 * (ps - 1)
+    return {
+        "fixed_pages": -(-pin // ps),
+        "rolling_pages": -(-(window + ps - 1 + total) // ps),
+        "private_pages": -(-(pieces + biggest) // ps),
+        "table_width": pin // ps + window // ps + -(-(pieces + biggest) // ps),
+        "list_stride": pieces,
+    }
+
+
+def causal_layout(table, private_pages, page_size: int, pin: int, window: int, committed: int,
+                  evicted: int, block_sizes, table_width: int, list_stride: int) -> dict:
+    """Per-block rows and slot lists for exact-window block-causal attention.
+
+    table          page ids of the sequence, [fixed pages | rolling pages].
+    private_pages  [num_blocks, P] page ids owned by each block.
+    committed      tokens already history (C); staged token t is position C + t.
+    evicted        rolling tokens rotated out of the table (multiple of
+                   page_size, at most window_evicted_tokens(...)).
+    block_sizes    staged tokens of each causal block, in order.
+
+    Returns int32 ``block_tables`` [nb, table_width] (unused entries -1),
+    ``n_ctx`` [nb] (keys before the block's own tokens) and ``seq_len`` [nb];
+    int64 ``stage_slots`` / ``stage_slots2`` [T] (the staged token's own slot
+    and its copy in its block's private pages, -1 if none); and int64
+    ``commit_src`` / ``commit_dst`` and ``current_src`` / ``current_dst``
+    [nb * list_stride] (block b's entries at b * list_stride, padded with -1):
+    copies of committed keys, made at commit, and of earlier blocks' staged
+    keys, made after every forward's scatter.
+    """
+    ps = int(page_size)
+    if ps < 1 or ps & (ps - 1):
+        raise ValueError("page_size must be a power of two")
+    if min(pin, window, committed, evicted) < 0 or evicted % ps:
+        raise ValueError("negative size or unaligned eviction")
+    if evicted > window_evicted_tokens(ps, pin, window, committed):
+        raise ValueError("eviction reaches into the next block's window")
+    table = [int(t) for t in np.asarray(table).reshape(-1)]
+    private_pages = np.asarray(private_pages).reshape(len(block_sizes), -1)
+    n_fixed = -(-pin // ps)
+    n_roll = len(table) - n_fixed
+    total = int(sum(block_sizes))
+    last = committed + total - 1
+    if n_roll < 0 or (last >= pin and (last - pin - evicted) // ps >= n_roll):
+        raise ValueError("table too short for the staged tokens")
+
+    def slot_of(x):
+        if x < pin:
+            return table[x // ps] * ps + x % ps
+        r = x - pin - evicted
+        return table[n_fixed + r // ps] * ps + r % ps
+
+    # Every page of the table with the logical positions it holds.
+    pages = []
+    for p in range(n_fixed):
+        pages.append((table[p], list(range(p * ps, min((p + 1) * ps, pin)))))
+    for j in range(n_roll):
+        q = evicted // ps + j
+        pages.append((table[n_fixed + j], list(range(pin + q * ps, pin + (q + 1) * ps))))
+
+    nb = len(block_sizes)
+    out = {
+        "block_tables": np.full((nb, table_width), -1, np.int32),
+        "n_ctx": np.zeros(nb, np.int32),
+        "seq_len": np.asarray(block_sizes, np.int32).copy(),
+        "stage_slots": np.zeros(total, np.int64),
+        "stage_slots2": np.full(total, -1, np.int64),
+    }
+    for name in ("commit_src", "commit_dst", "current_src", "current_dst"):
+        out[name] = np.full(nb * list_stride, -1, np.int64)
+
+    start = committed
+    for b, size in enumerate(block_sizes):
+        end = start + int(size)
+        seen = set(visible_keys(start, end, pin, window))
+        full = [pid for pid, pos in pages
+                if len(pos) == ps and all(x in seen and x < start for x in pos)]
+        on_full = {x for pid, pos in pages if pid in full for x in pos}
+        pieces = [x for x in sorted(seen) if x < start and x not in on_full]
+        direct = not pieces and start >= pin and (start - pin) % ps == 0
+        if direct:
+            own_pages = [pid for pid, pos in pages if pos and start <= pos[0] < end]
+            row = full + own_pages
+        else:
+            n_priv = -(-(len(pieces) + int(size)) // ps)
+            if n_priv > private_pages.shape[1]:
+                raise ValueError("too few private pages")
+            row = full + [int(p) for p in private_pages[b, :n_priv]]
+        if len(row) > table_width:
+            raise ValueError("table_width too small")
+        out["block_tables"][b, :len(row)] = row
+        out["n_ctx"][b] = len(full) * ps + len(pieces)
+
+        def private_slot(k):
+            return int(private_pages[b, k // ps]) * ps + k % ps
+
+        committed_pieces = [(k, x) for k, x in enumerate(pieces) if x < committed]
+        current_pieces = [(k, x) for k, x in enumerate(pieces) if x >= committed]
+        for lists, chosen in ((("commit_src", "commit_dst"), committed_pieces),
+                              (("current_src", "current_dst"), current_pieces)):
+            if len(chosen) > list_stride:
+                raise ValueError("list_stride too small")
+            for i, (k, x) in enumerate(chosen):
+                out[lists[0]][b * list_stride + i] = slot_of(x)
+                out[lists[1]][b * list_stride + i] = private_slot(k)
+        for i in range(int(size)):
+            t = start - committed + i
+            out["stage_slots"][t] = slot_of(start + i)
+            if not direct:
+                out["stage_slots2"][t] = private_slot(len(pieces) + i)
+        start = end
+    return out

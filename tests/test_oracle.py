@@ -446,3 +446,170 @@ def test_copy_slots_matches_fancy_indexing_and_skips_sentinels():
     # sentinel destinations and untouched slots keep their bytes
     untouched = np.setdiff1d(np.arange(pages * ps), dst[keep])
     assert np.array_equal(got.reshape(layers, -1, h, d)[:, untouched], pool.reshape(layers, -1, h, d)[:, untouched])
+
+
+# --------------------------------------------------------------------------- exact-window layout
+
+LAYOUT_KEYS = ("block_tables", "n_ctx", "seq_len", "stage_slots", "stage_slots2",
+               "commit_src", "commit_dst", "current_src", "current_dst")
+
+
+def _layout_cases():
+    import json
+    with open(os.path.join(GOLDEN, "causal_layout.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _layout_cases(), ids=lambda c: c["name"])
+def test_causal_layout_hand_worked_fixtures(case):
+    out = orc.causal_layout(case["table"], case["private_pages"], case["page_size"], case["pin"],
+                            case["window"], case["committed"], case["evicted"], case["block_sizes"],
+                            case["table_width"], case["list_stride"])
+    for key in LAYOUT_KEYS:
+        assert out[key].tolist() == np.asarray(case[key]).reshape(out[key].shape).tolist(), key
+
+
+def _forward(pool, lay, committed, ps, block_sizes):
+    """Drive a pool of logical positions with a layout's slot lists only, then
+    read every block's keys back through its row; returns the key lists."""
+    for s, d in zip(lay["commit_src"], lay["commit_dst"]):
+        if s >= 0 and d >= 0:
+            pool[d] = pool[s]
+    for t, (s1, s2) in enumerate(zip(lay["stage_slots"], lay["stage_slots2"])):
+        pool[s1] = committed + t
+        if s2 >= 0:
+            pool[s2] = committed + t
+    for s, d in zip(lay["current_src"], lay["current_dst"]):
+        if s >= 0 and d >= 0:
+            pool[d] = pool[s]
+    keys = []
+    for b, size in enumerate(block_sizes):
+        n = int(lay["n_ctx"][b]) + int(size)
+        row = lay["block_tables"][b]
+        keys.append([int(pool[int(row[j // ps]) * ps + j % ps]) for j in range(n)])
+    return keys
+
+
+def _check_window(keys, committed, block_sizes, pin, window):
+    start = committed
+    for b, size in enumerate(block_sizes):
+        end = start + size
+        want = set(range(min(pin, end))) | set(range(max(pin, start - window), end))
+        got = keys[b]
+        assert len(got) == len(set(got)), f"block {b}: a key is read twice"
+        assert set(got) == want, f"block {b}: read {sorted(set(got) ^ want)} wrongly"
+        assert got[len(got) - size:] == list(range(start, end)), f"block {b}: own keys not last"
+        start = end
+
+
+GEOMETRIES = [
+    # page_size, pin, window, block_sizes, commit sizes
+    (4, 6, 7, [2, 5], [7, 7, 2, 7, 7, 7]),
+    (4, 4, 8, [4, 4], [8, 8, 8, 4, 8]),
+    (8, 0, 19, [3, 3, 3], [9, 9, 9, 9, 9, 3, 9]),
+    (16, 37, 50, [13, 13, 13], [39] * 6),
+    (8, 8, 0, [5, 6], [11] * 5),
+    (32, 96, 64, [32, 32], [64] * 5),
+    (2, 3, 5, [1, 2, 1], [4, 4, 1, 4, 4, 4]),
+    (16, 21, 200, [7, 30, 3], [40, 40, 40, 40, 40, 40]),
+]
+
+
+@pytest.mark.parametrize("geometry", GEOMETRIES, ids=lambda g: f"ps{g[0]}_pin{g[1]}_w{g[2]}")
+def test_causal_layout_rollout_reads_exactly_the_window(geometry):
+    """A rollout from an empty cache: forwards write only through the layout's
+    slot lists, commits evict by rotating the rolling part of the table.  Every
+    block must read its fixed region, its window and itself, each key once,
+    its own keys last."""
+    ps, pin, window, sizes, commits = geometry
+    bounds = orc.causal_layout_bounds(ps, pin, window, sizes)
+    n_fixed, n_roll, n_priv = bounds["fixed_pages"], bounds["rolling_pages"], bounds["private_pages"]
+    rng = np.random.default_rng(ps * 1000 + pin)
+    ids = rng.permutation(n_fixed + n_roll + len(sizes) * n_priv + 5)
+    table = ids[:n_fixed + n_roll].copy()
+    private = ids[n_fixed + n_roll:n_fixed + n_roll + len(sizes) * n_priv].reshape(len(sizes), n_priv)
+    pool = np.full((len(ids) + 1) * ps, -1, np.int64)
+    committed = evicted = 0
+    for n in commits:
+        lay = orc.causal_layout(table, private, ps, pin, window, committed, evicted, sizes,
+                                bounds["table_width"], bounds["list_stride"])
+        for _ in range(2):     # several denoising forwards between commits
+            _check_window(_forward(pool, lay, committed, ps, sizes), committed, sizes, pin, window)
+        committed += n
+        new_evicted = orc.window_evicted_tokens(ps, pin, window, committed)
+        shift = (new_evicted - evicted) // ps
+        table = np.concatenate([table[:n_fixed], orc.rotate_rows(table[None, n_fixed:], shift)[0]])
+        evicted = new_evicted
+
+
+def test_causal_layout_read_back_catches_a_page_aligned_window():
+    """The read-back check is strong enough to see the error the exact layout
+    removes: a block that reads its window from the start of the window-start
+    page sees keys outside its window."""
+    case = _layout_cases()[0]
+    lay = orc.causal_layout(case["table"], case["private_pages"], case["page_size"], case["pin"],
+                            case["window"], case["committed"], case["evicted"], case["block_sizes"],
+                            case["table_width"], case["list_stride"])
+    ps = case["page_size"]
+    pool = np.full(64 * ps, -1, np.int64)
+    # committed keys already sit at their own slots
+    table = case["table"]
+    for x in range(case["committed"]):
+        if x < case["pin"]:
+            pool[table[x // ps] * ps + x % ps] = x
+        elif x - case["pin"] >= case["evicted"]:
+            r = x - case["pin"] - case["evicted"]
+            pool[table[2 + r // ps] * ps + r % ps] = x
+    keys = _forward(pool.copy(), lay, case["committed"], ps, case["block_sizes"])
+    _check_window(keys, case["committed"], case["block_sizes"], case["pin"], case["window"])
+    # Block 0 reading the whole window-start page (id 10) instead of its piece.
+    bad = dict(lay)
+    bad["block_tables"] = lay["block_tables"].copy()
+    bad["block_tables"][0, :3] = [7, 10, 11]
+    bad["n_ctx"] = lay["n_ctx"].copy()
+    bad["n_ctx"][0] = 12
+    keys = _forward(pool.copy(), bad, case["committed"], ps, case["block_sizes"])
+    with pytest.raises(AssertionError):
+        _check_window(keys, case["committed"], case["block_sizes"], case["pin"], case["window"])
+
+
+def test_causal_layout_bounds_hold_and_lists_split_by_commit_point():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        ps = int(2 ** rng.integers(0, 6))
+        pin = int(rng.integers(0, 4 * ps + 3))
+        window = int(rng.integers(0, 6 * ps + 3))
+        sizes = [int(v) for v in rng.integers(1, 3 * ps + 2, size=int(rng.integers(1, 5)))]
+        committed = int(rng.integers(0, pin + window + 10 * ps))
+        evicted = orc.window_evicted_tokens(ps, pin, window, committed)
+        bounds = orc.causal_layout_bounds(ps, pin, window, sizes)
+        n_tab = bounds["fixed_pages"] + bounds["rolling_pages"]
+        table = np.arange(n_tab)
+        private = n_tab + np.arange(len(sizes) * bounds["private_pages"]).reshape(len(sizes), -1)
+        lay = orc.causal_layout(table, private, ps, pin, window, committed, evicted, sizes,
+                                bounds["table_width"], bounds["list_stride"])
+        # committed copies read committed keys only, current copies staged ones
+        src_pos = {}
+        for x in range(committed + sum(sizes)):
+            if x < pin:
+                src_pos[int(table[x // ps]) * ps + x % ps] = x
+            elif x - pin >= evicted:
+                r = x - pin - evicted
+                src_pos[int(table[bounds["fixed_pages"] + r // ps]) * ps + r % ps] = x
+        assert all(src_pos[s] < committed for s in lay["commit_src"] if s >= 0)
+        assert all(src_pos[s] >= committed for s in lay["current_src"] if s >= 0)
+        assert sorted(src_pos[s] for s in lay["stage_slots"]) == list(range(committed, committed + sum(sizes)))
+        # destinations are private slots, each written once
+        dst = [d for d in np.concatenate([lay["commit_dst"], lay["current_dst"], lay["stage_slots2"]]) if d >= 0]
+        assert len(dst) == len(set(dst)) and all(d // ps >= n_tab for d in dst)
+
+
+def test_causal_layout_rejects_what_it_cannot_lay_out():
+    case = _layout_cases()[0]
+    args = dict(table=case["table"], private_pages=case["private_pages"], page_size=4, pin=6, window=7,
+                committed=19, evicted=4, block_sizes=[2, 5], table_width=6, list_stride=9)
+    orc.causal_layout(**args)
+    for change in (dict(page_size=3), dict(evicted=8), dict(evicted=2), dict(table_width=4),
+                   dict(table=case["table"][:4]), dict(block_sizes=[2, 13])):
+        with pytest.raises(ValueError):
+            orc.causal_layout(**{**args, **change})

@@ -278,6 +278,108 @@ pkv_status pkv_rotate_rows(void* data, int64_t rows, int64_t cols, int64_t row_s
 pkv_status pkv_copy_slots(const pkv_pool* pool, int32_t num_layers, int64_t layer_stride, const int64_t* src_slots,
                           const int64_t* dst_slots, int64_t n, hipStream_t stream);
 
+/*
+ * Exact-window layout.
+ * [P1] Description / Cache (the sequence is [fixed region | rolling history
+ * window | staged tokens]; a table row can start a key sequence only at a
+ * page boundary, so each causal block gets private pages at the end of its
+ * row holding the visible keys of the up to three partly visible pages --
+ * fixed-region tail, window-start page, earlier keys on the block's start
+ * page -- and then its own tokens, which stay the last keys of its row; at
+ * commit one kernel reads the table and rewrites every per-block tensor in
+ * place) and the review thread on the private regions (committed keys are
+ * copied at commit, earlier blocks' staged keys every forward; at most
+ * 3 (page_size - 1) copied keys per block).
+ *
+ * Geometry (logical key positions):
+ *   - keys [0, committed) are history, staged token t is key committed + t;
+ *   - the fixed region is [0, pin_tokens) and owns the first
+ *     fixed_pages = ceil(pin_tokens / page_size) table entries;
+ *   - the rolling region (keys >= pin_tokens) starts on a page of its own;
+ *     the first `evicted` rolling tokens (whole pages) have been rotated out
+ *     of the table, so rolling key x is on table entry
+ *     fixed_pages + (x - pin_tokens - evicted) / page_size;
+ *   - causal block b covers keys [s_b, s_b + block_sizes[b]), s_0 = committed,
+ *     and sees [0, pin_tokens), [max(pin_tokens, s_b - window_tokens), s_b)
+ *     and itself.
+ * Commit sequence: after `committed` grows, evicted' =
+ * pkv_window_evicted_tokens(...) and the rolling part of the table is rotated
+ * left by (evicted' - evicted) / page_size entries (pkv_rotate_rows); then
+ * pkv_causal_layout, then pkv_copy_slots over the commit list.  Each forward:
+ * pkv_scatter_slots with (stage_slots, stage_slots2), pkv_copy_slots over the
+ * current list, then attention over block_tables (one batch entry per causal
+ * block: n_ctx keys before the block, seq_len new keys).
+ */
+typedef struct {
+  int32_t fixed_pages;    /* table entries of the fixed region                       */
+  int32_t rolling_pages;  /* rolling entries that always cover window and staged keys */
+  int32_t private_pages;  /* private pages each causal block needs                   */
+  int32_t table_width;    /* entries of a per-block row                              */
+  int32_t list_stride;    /* commit / current list entries per block = 3 (ps - 1)    */
+} pkv_causal_bounds;
+
+#define PKV_MAX_CAUSAL_BLOCKS 64
+
+/*
+ * pkv_causal_layout_bounds -- sizes an exact-window geometry needs (host only).
+ *   rolling_pages = ceil((window + page_size - 1 + sum(block_sizes)) / page_size)
+ *   private_pages = ceil((3 (page_size - 1) + max(block_sizes)) / page_size)
+ *   table_width   = pin / page_size + window / page_size + private_pages
+ * Errors: NULL -> PKV_ERR_NULL; page_size not a power of two, negative
+ * sizes, a block size < 1, num_blocks outside 1..PKV_MAX_CAUSAL_BLOCKS or a
+ * size beyond int32 -> PKV_ERR_SHAPE.
+ */
+pkv_status pkv_causal_layout_bounds(int32_t page_size, int64_t pin_tokens, int64_t window_tokens,
+                                    const int32_t* block_sizes, int32_t num_blocks, pkv_causal_bounds* bounds);
+
+/*
+ * pkv_window_evicted_tokens -- rolling tokens no later block can see, in
+ * whole pages (host only): floor(max(0, committed - window - pin) / ps) * ps.
+ * Returns -1 for a page size that is not a power of two or a negative size.
+ */
+int64_t pkv_window_evicted_tokens(int32_t page_size, int64_t pin_tokens, int64_t window_tokens, int64_t committed);
+
+/*
+ * pkv_causal_layout -- rewrite every per-block tensor of an exact-window
+ * geometry from the sequence's page table (one launch, no host data).
+ *
+ *   table          device int32 [table_len]: fixed pages, then rolling pages.
+ *   private_pages  device int32 [num_blocks, private_stride]: pages owned by
+ *                  each causal block, disjoint from the table's.
+ *   block_sizes    HOST int32 [num_blocks] (values >= 1, num_blocks <= 64);
+ *                  passed by value to the kernel.
+ *   block_tables   device int32 [num_blocks, table_width]: block b's whole
+ *                  visible pages (keys all visible and before the block), in
+ *                  key order, then its private pages; a block with no other
+ *                  visible key whose first key starts a rolling page reads
+ *                  its own keys from their own pages instead.  Unused entries
+ *                  are -1.
+ *   n_ctx, seq_len device int32 [num_blocks]: keys before the block's own
+ *                  tokens in its row, and block_sizes[b].
+ *   stage_slots    device int64 [sum(block_sizes)]: staged token t's slot in
+ *                  the sequence's own pages; stage_slots2: its copy in its
+ *                  block's private pages (after the block's copied keys), or
+ *                  -1 when the block reads its own pages.
+ *   commit_src/dst device int64 [num_blocks * list_stride]: block b's entries
+ *   current_src/dst start at b * list_stride, padded with -1 sentinels.  The
+ *                  private pages hold the copied keys in key order; those
+ *                  before `committed` are in the commit list, the others
+ *                  (earlier blocks' staged keys) in the current list.
+ *                  With list_stride 0 (page size 1) they may be NULL.
+ * Every output is written whole (padding included); nothing else is touched.
+ * Errors: NULL -> PKV_ERR_NULL; a bad geometry (as pkv_causal_layout_bounds),
+ * evicted not a multiple of page_size or beyond pkv_window_evicted_tokens,
+ * a table too short for the staged keys, private_stride / table_width /
+ * list_stride below pkv_causal_layout_bounds, or keys beyond int32 ->
+ * PKV_ERR_SHAPE.  Page ids are not checked.
+ */
+pkv_status pkv_causal_layout(const int32_t* table, int32_t table_len, const int32_t* private_pages,
+                             int32_t private_stride, int32_t page_size, int64_t pin_tokens, int64_t window_tokens,
+                             int64_t committed, int64_t evicted, const int32_t* block_sizes, int32_t num_blocks,
+                             int32_t* block_tables, int32_t table_width, int32_t* n_ctx, int32_t* seq_len,
+                             int64_t* stage_slots, int64_t* stage_slots2, int64_t* commit_src, int64_t* commit_dst,
+                             int64_t* current_src, int64_t* current_dst, int32_t list_stride, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,13 +29,19 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
 
 EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
             "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
-            "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots"]
+            "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
+            "pkv_window_evicted_tokens", "pkv_causal_layout"]
 
 
 class PkvError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({text})")
         self.status = status
+
+
+class PkvCausalBounds(ctypes.Structure):
+    _fields_ = [("fixed_pages", ctypes.c_int32), ("rolling_pages", ctypes.c_int32),
+                ("private_pages", ctypes.c_int32), ("table_width", ctypes.c_int32), ("list_stride", ctypes.c_int32)]
 
 
 class PkvPoolStruct(ctypes.Structure):
@@ -71,6 +77,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
         "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
         "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
+        "pkv_causal_layout_bounds": (ctypes.c_int, [I32, I64, I64, P, I32, ctypes.POINTER(PkvCausalBounds)]),
+        "pkv_window_evicted_tokens": (I64, [I32, I64, I64, I64]),
+        "pkv_causal_layout": (ctypes.c_int, [P, I32, P, I32, I32, I64, I64, I64, I64, P, I32, P, I32, P, P, P, P,
+                                             P, P, P, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -229,3 +239,63 @@ def pkv_copy_slots(pool: Pool, src_slots: torch.Tensor, dst_slots: torch.Tensor,
     _check("pkv_copy_slots", load_library().pkv_copy_slots(
         ctypes.byref(ps), num_layers, layer_stride, src_slots.data_ptr(), dst_slots.data_ptr(), src_slots.numel(),
         _stream(stream)))
+
+
+def _host_block_sizes(block_sizes):
+    sizes = [int(v) for v in block_sizes]
+    return (ctypes.c_int32 * max(1, len(sizes)))(*sizes), len(sizes)
+
+
+def pkv_causal_layout_bounds(page_size: int, pin_tokens: int, window_tokens: int, block_sizes) -> dict:
+    """Table, private-page and list sizes an exact-window geometry needs."""
+    arr, n = _host_block_sizes(block_sizes)
+    out = PkvCausalBounds()
+    _check("pkv_causal_layout_bounds", load_library().pkv_causal_layout_bounds(
+        page_size, pin_tokens, window_tokens, arr, n, ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in PkvCausalBounds._fields_}
+
+
+def pkv_window_evicted_tokens(page_size: int, pin_tokens: int, window_tokens: int, committed: int) -> int:
+    """Rolling tokens (whole pages) that no block after ``committed`` can see."""
+    v = load_library().pkv_window_evicted_tokens(page_size, pin_tokens, window_tokens, committed)
+    if v < 0:
+        raise ValueError("bad geometry")
+    return v
+
+
+class CausalLayout:
+    """Device tensors of one exact-window geometry, written in place by
+    ``pkv_causal_layout`` (fixed addresses across commits)."""
+
+    def __init__(self, page_size: int, pin_tokens: int, window_tokens: int, block_sizes, device="cuda"):
+        self.page_size, self.pin_tokens, self.window_tokens = page_size, pin_tokens, window_tokens
+        self.block_sizes = [int(v) for v in block_sizes]
+        self.bounds = pkv_causal_layout_bounds(page_size, pin_tokens, window_tokens, self.block_sizes)
+        nb, total = len(self.block_sizes), sum(self.block_sizes)
+        i32, i64 = dict(dtype=torch.int32, device=device), dict(dtype=torch.int64, device=device)
+        self.block_tables = torch.empty((nb, self.bounds["table_width"]), **i32)
+        self.n_ctx = torch.empty(nb, **i32)
+        self.seq_len = torch.empty(nb, **i32)
+        self.stage_slots = torch.empty(total, **i64)
+        self.stage_slots2 = torch.empty(total, **i64)
+        ls = nb * self.bounds["list_stride"]
+        self.commit_src, self.commit_dst = torch.empty(ls, **i64), torch.empty(ls, **i64)
+        self.current_src, self.current_dst = torch.empty(ls, **i64), torch.empty(ls, **i64)
+
+
+def pkv_causal_layout(layout: CausalLayout, table: torch.Tensor, private_pages: torch.Tensor, committed: int,
+                      evicted: int, stream=None) -> None:
+    """Rewrite ``layout``'s tensors from the int32 page table of the sequence
+    and the int32 [num_blocks, P] private pages of its causal blocks."""
+    if table.dtype != torch.int32 or private_pages.dtype != torch.int32 or private_pages.dim() != 2:
+        raise ValueError("table and private_pages must be int32; private_pages [num_blocks, P]")
+    if not table.is_contiguous() or private_pages.stride(1) != 1:
+        raise ValueError("table and private_pages rows must be contiguous")
+    arr, n = _host_block_sizes(layout.block_sizes)
+    L = layout
+    _check("pkv_causal_layout", load_library().pkv_causal_layout(
+        table.data_ptr(), table.numel(), private_pages.data_ptr(), private_pages.stride(0), L.page_size,
+        L.pin_tokens, L.window_tokens, committed, evicted, arr, n, L.block_tables.data_ptr(),
+        L.block_tables.shape[1], L.n_ctx.data_ptr(), L.seq_len.data_ptr(), L.stage_slots.data_ptr(),
+        L.stage_slots2.data_ptr(), L.commit_src.data_ptr(), L.commit_dst.data_ptr(), L.current_src.data_ptr(),
+        L.current_dst.data_ptr(), L.bounds["list_stride"], _stream(stream)))

@@ -13,6 +13,7 @@ namespace {
 using namespace pkv;
 
 constexpr int kAbiVersion = 1;
+static_assert(kMaxCausalBlocks == PKV_MAX_CAUSAL_BLOCKS, "block limit of the ABI and the kernel differ");
 
 // Key splits of the decode: chunks of at least 512 tokens and at most 16
 // splits ("Support shared-prefix attention for n-sample requests in FMHA",
@@ -87,6 +88,35 @@ int device_cu_count() {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+// Sizes an exact-window geometry needs (see pkv_causal_layout_bounds).
+bool window_sizes(int32_t page_size, int64_t pin, int64_t window, const int32_t* block_sizes, int32_t num_blocks,
+                  pkv_causal_bounds* out, int64_t* total) {
+  if (!is_pow2(page_size) || pin < 0 || window < 0 || !block_sizes) return false;
+  if (num_blocks < 1 || num_blocks > kMaxCausalBlocks) return false;
+  int64_t sum = 0, biggest = 0;
+  for (int i = 0; i < num_blocks; ++i) {
+    if (block_sizes[i] < 1) return false;
+    sum += block_sizes[i];
+    biggest = std::max<int64_t>(biggest, block_sizes[i]);
+  }
+  const int64_t ps = page_size, pieces = 3 * (ps - 1);
+  const int64_t fixed = ceil_div(pin, ps), rolling = ceil_div(window + ps - 1 + sum, ps);
+  const int64_t priv = ceil_div(pieces + biggest, ps), width = pin / ps + window / ps + priv;
+  if (fixed + rolling > INT32_MAX || width > INT32_MAX || pieces > INT32_MAX) return false;
+  out->fixed_pages = (int32_t)fixed;
+  out->rolling_pages = (int32_t)rolling;
+  out->private_pages = (int32_t)priv;
+  out->table_width = (int32_t)width;
+  out->list_stride = (int32_t)pieces;
+  *total = sum;
+  return true;
+}
+
+int64_t evicted_tokens(int64_t ps, int64_t pin, int64_t window, int64_t committed) {
+  const int64_t first_needed = std::max<int64_t>(0, committed - window - pin);
+  return first_needed / ps * ps;
 }
 
 }  // namespace
@@ -405,6 +435,72 @@ pkv_status pkv_copy_slots(const pkv_pool* pool, int32_t num_layers, int64_t laye
   p.num_layers = num_layers;
   p.vecs_per_row = (int32_t)(row_b / vec);
   return launch_copy_slots(p, vec, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+pkv_status pkv_causal_layout_bounds(int32_t page_size, int64_t pin_tokens, int64_t window_tokens,
+                                    const int32_t* block_sizes, int32_t num_blocks, pkv_causal_bounds* bounds) {
+  if (!block_sizes || !bounds) return PKV_ERR_NULL;
+  int64_t total = 0;
+  return window_sizes(page_size, pin_tokens, window_tokens, block_sizes, num_blocks, bounds, &total) ? PKV_OK
+                                                                                                    : PKV_ERR_SHAPE;
+}
+
+int64_t pkv_window_evicted_tokens(int32_t page_size, int64_t pin_tokens, int64_t window_tokens, int64_t committed) {
+  if (!is_pow2(page_size) || pin_tokens < 0 || window_tokens < 0 || committed < 0) return -1;
+  return evicted_tokens(page_size, pin_tokens, window_tokens, committed);
+}
+
+pkv_status pkv_causal_layout(const int32_t* table, int32_t table_len, const int32_t* private_pages,
+                             int32_t private_stride, int32_t page_size, int64_t pin_tokens, int64_t window_tokens,
+                             int64_t committed, int64_t evicted, const int32_t* block_sizes, int32_t num_blocks,
+                             int32_t* block_tables, int32_t table_width, int32_t* n_ctx, int32_t* seq_len,
+                             int64_t* stage_slots, int64_t* stage_slots2, int64_t* commit_src, int64_t* commit_dst,
+                             int64_t* current_src, int64_t* current_dst, int32_t list_stride, hipStream_t stream) {
+  if (!block_sizes) return PKV_ERR_NULL;
+  pkv_causal_bounds need;
+  int64_t total = 0;
+  if (!window_sizes(page_size, pin_tokens, window_tokens, block_sizes, num_blocks, &need, &total))
+    return PKV_ERR_SHAPE;
+  if (!table || !private_pages || !block_tables || !n_ctx || !seq_len || !stage_slots || !stage_slots2)
+    return PKV_ERR_NULL;
+  if (list_stride > 0 && (!commit_src || !commit_dst || !current_src || !current_dst)) return PKV_ERR_NULL;
+  const int64_t ps = page_size;
+  if (committed < 0 || evicted < 0 || evicted % ps != 0) return PKV_ERR_SHAPE;
+  if (evicted > evicted_tokens(ps, pin_tokens, window_tokens, committed)) return PKV_ERR_SHAPE;
+  // every staged key must have a page in the table
+  const int64_t n_fixed = need.fixed_pages, last = committed + total - 1;
+  if (table_len < n_fixed) return PKV_ERR_SHAPE;
+  if (last >= pin_tokens && (last - pin_tokens - evicted) / ps >= table_len - n_fixed) return PKV_ERR_SHAPE;
+  if (private_stride < need.private_pages || table_width < need.table_width || list_stride < need.list_stride)
+    return PKV_ERR_SHAPE;
+  if (committed + total > INT32_MAX) return PKV_ERR_SHAPE;
+  LayoutParams p;
+  p.table = table;
+  p.priv = private_pages;
+  p.priv_stride = private_stride;
+  p.n_fixed = (int32_t)n_fixed;
+  p.ps_shift = log2i(ps);
+  p.num_blocks = num_blocks;
+  p.pin = pin_tokens;
+  p.window = window_tokens;
+  p.committed = committed;
+  p.evicted = evicted;
+  p.block_start[0] = committed;
+  for (int i = 0; i < num_blocks; ++i) p.block_start[i + 1] = p.block_start[i] + block_sizes[i];
+  for (int i = num_blocks + 1; i <= kMaxCausalBlocks; ++i) p.block_start[i] = p.block_start[num_blocks];
+  p.block_tables = block_tables;
+  p.table_width = table_width;
+  p.list_stride = list_stride;
+  p.n_ctx = n_ctx;
+  p.seq_len = seq_len;
+  p.stage_slots = stage_slots;
+  p.stage_slots2 = stage_slots2;
+  p.commit_src = commit_src;
+  p.commit_dst = commit_dst;
+  p.current_src = current_src;
+  p.current_dst = current_dst;
+  return launch_causal_layout(p, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 }  // extern "C"

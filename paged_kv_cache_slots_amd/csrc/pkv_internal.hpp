@@ -135,6 +135,30 @@ struct CopySlotsParams {
   int32_t vecs_per_row;       // row_b / vec_bytes
 };
 
+// Exact-window per-block layout (one workgroup per causal block).
+constexpr int kMaxCausalBlocks = 64;
+struct LayoutParams {
+  const int32_t* table;       // [n_fixed + rolling pages]
+  const int32_t* priv;        // [num_blocks, priv_stride]
+  int32_t priv_stride;
+  int32_t n_fixed;
+  int32_t ps_shift;
+  int32_t num_blocks;
+  int64_t pin, window, committed, evicted;
+  int64_t block_start[kMaxCausalBlocks + 1];   // committed + prefix sums of the block sizes
+  int32_t* block_tables;
+  int32_t table_width;
+  int32_t list_stride;
+  int32_t* n_ctx;
+  int32_t* seq_len;
+  int64_t* stage_slots;
+  int64_t* stage_slots2;
+  int64_t* commit_src;
+  int64_t* commit_dst;
+  int64_t* current_src;
+  int64_t* current_dst;
+};
+
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);
@@ -145,6 +169,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);
 hipError_t launch_copy_slots(const CopySlotsParams& p, int vec_bytes, hipStream_t stream);
+hipError_t launch_causal_layout(const LayoutParams& p, hipStream_t stream);
 int64_t prefill_units(int32_t batch, int32_t s_q, int32_t num_q_heads);
 size_t prefill_slot_bytes();
 

@@ -150,3 +150,45 @@ def test_copy_slots_argument_checks():
     assert lib.pkv_copy_slots(ctypes.byref(p), 1, 0, None, None, 0, None) == 0
     bad = _pool(page_size=48)
     assert lib.pkv_copy_slots(ctypes.byref(bad), 1, 0, A, A, 4, None) == 2
+
+
+def test_causal_layout_host_sizes_match_the_oracle():
+    import numpy as np
+    import oracle as orc
+    rng = np.random.default_rng(2)
+    for _ in range(300):
+        ps = int(2 ** rng.integers(0, 8))
+        pin, window = int(rng.integers(0, 6 * ps + 5)), int(rng.integers(0, 9 * ps + 5))
+        sizes = [int(v) for v in rng.integers(1, 4 * ps + 3, size=int(rng.integers(1, 65)))]
+        assert pkv.pkv_causal_layout_bounds(ps, pin, window, sizes) == orc.causal_layout_bounds(ps, pin, window,
+                                                                                                sizes)
+        committed = int(rng.integers(0, 20 * ps + pin + window))
+        assert pkv.pkv_window_evicted_tokens(ps, pin, window, committed) == orc.window_evicted_tokens(
+            ps, pin, window, committed)
+    lib = pkv.load_library()
+    assert lib.pkv_window_evicted_tokens(24, 0, 0, 100) == -1
+    assert lib.pkv_window_evicted_tokens(16, -1, 0, 100) == -1
+
+
+def _layout_call(**kw):
+    """pkv_causal_layout of the first hand-worked geometry (page size 4, pin 6,
+    window 7, committed 19, evicted 4, blocks [2, 5]), fake device pointers."""
+    a = dict(table=A, table_len=7, priv=A, priv_stride=4, ps=4, pin=6, window=7, committed=19, evicted=4,
+             sizes=[2, 5], bt=A, width=6, n_ctx=A, seq_len=A, st=A, st2=A, cs=A, cd=A, us=A, ud=A, ls=9)
+    a.update(kw)
+    sizes = (ctypes.c_int32 * max(1, len(a["sizes"])))(*a["sizes"])
+    return pkv.load_library().pkv_causal_layout(
+        a["table"], a["table_len"], a["priv"], a["priv_stride"], a["ps"], a["pin"], a["window"], a["committed"],
+        a["evicted"], sizes, len(a["sizes"]), a["bt"], a["width"], a["n_ctx"], a["seq_len"], a["st"], a["st2"],
+        a["cs"], a["cd"], a["us"], a["ud"], a["ls"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(table=None), 1), (dict(priv=None), 1), (dict(cd=None), 1), (dict(st2=None), 1), (dict(us=None), 1),
+    (dict(ps=6), 2), (dict(pin=-1), 2), (dict(evicted=2), 2), (dict(evicted=8), 2), (dict(committed=-1), 2),
+    (dict(table_len=5), 2), (dict(table_len=1), 2), (dict(priv_stride=3), 2), (dict(width=5), 2), (dict(ls=8), 2),
+    (dict(sizes=[]), 2), (dict(sizes=[2, 0]), 2), (dict(sizes=[1] * 65), 2), (dict(sizes=[2, 13]), 2),
+    (dict(committed=2 ** 31 - 3, pin=0, window=2 ** 31), 2),
+])
+def test_causal_layout_argument_checks(kw, expect):
+    assert _layout_call(**kw) == expect

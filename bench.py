@@ -138,7 +138,7 @@ def time_events(torch, step, reps, flush=None):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
-# ----------------------------------------------------------------------------- headline: config 2
+# ----------------------------------------------------------------------------- headline: bf16 GQA paged decode
 
 def setup_decode_case(case, torch, pkv):
     pool = pkv.Pool(to_dev(case.pool.k, torch), to_dev(case.pool.v, torch),
@@ -313,6 +313,56 @@ def run_long_fp8(torch, pkv, W, flush):
             "frac_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
+def commit_sequence(torch, pkv, flush):
+    """One exact-window commit and one layer's forward-side writes at the
+    block-causal prefill's geometry: fixed region 1024, window 4096, a
+    1560-token chunk cut into three 520-token causal blocks, 32-token pages,
+    24 kv heads x 128 bf16, 30 layers.  Commit = rotate the rolling table +
+    lay out the blocks + copy committed keys into private pages (every
+    layer); forward writes = scatter the chunk to its slots and private copies
+    + copy earlier blocks' keys (one layer)."""
+    ps, pin, window, sizes, layers, hkv, d = 32, 1024, 4096, [520, 520, 520], 30, 24, 128
+    lay = pkv.CausalLayout(ps, pin, window, sizes, device="cuda:0")
+    b = lay.bounds
+    n_tab = b["fixed_pages"] + b["rolling_pages"]
+    n_pages = n_tab + len(sizes) * b["private_pages"]
+    ids = torch.randperm(n_pages, generator=torch.Generator().manual_seed(9)).to(torch.int32)
+    table = ids[:n_tab].to("cuda:0")
+    priv = ids[n_tab:].view(len(sizes), -1).to("cuda:0")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(10)
+    k = torch.randn((layers, n_pages, ps, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    v = torch.randn((layers, n_pages, ps, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    pool = pkv.Pool(k[0], v[0])
+    layer_stride = n_pages * ps * hkv * d
+    committed = pin + window + 3 * 1560 + 17          # steady state, chunk start off a page boundary
+    evicted = pkv.pkv_window_evicted_tokens(ps, pin, window, committed)
+    shift = (evicted - pkv.pkv_window_evicted_tokens(ps, pin, window, committed - 1560)) // ps
+    total = sum(sizes)
+    new_k = torch.randn((total, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    new_v = torch.randn((total, hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+
+    def commit():
+        pkv.pkv_rotate_rows(table[b["fixed_pages"]:], shift)
+        pkv.pkv_causal_layout(lay, table, priv, committed, evicted)
+        pkv.pkv_copy_slots(pool, lay.commit_src, lay.commit_dst, layers, layer_stride)
+
+    def forward_writes():
+        pkv.pkv_scatter_slots(pool, new_k, new_v, lay.stage_slots, slots2=lay.stage_slots2)
+        pkv.pkv_copy_slots(pool, lay.current_src, lay.current_dst)
+
+    for _ in range(3):
+        commit()
+        forward_writes()
+    cmed, cp10, cp90 = time_events(torch, commit, 30, flush)
+    fmed, fp10, fp90 = time_events(torch, forward_writes, 30, flush)
+    n_commit = int((lay.commit_src >= 0).sum())
+    n_current = int((lay.current_src >= 0).sum())
+    return {"commit_ms": cmed, "commit_ms_p10_p90": [cp10, cp90], "commit_copied_keys": n_commit,
+            "forward_writes_ms": fmed, "forward_writes_ms_p10_p90": [fp10, fp90],
+            "forward_current_copied_keys": n_current, "launches_per_commit": 3, "launches_per_forward_layer": 2}
+
+
 def run_commit(torch, pkv, W, flush):
     """Exact-window commit ops at the block-causal prefill's geometry (24 kv
     heads x 128, bf16, 32-token pages, 512-page pool): a private-page fill of
@@ -343,8 +393,10 @@ def run_commit(torch, pkv, W, flush):
     for _ in range(3):
         rot()
     rmed, _, _ = time_events(torch, rot, 30, flush)
+    seq = commit_sequence(torch, pkv, flush)
     return {"workload": "exact-window commit: private-page fill of 2048 slots x 8 layers (24 kv heads x 128, bf16, "
                         "32-token pages) and the rotation of a 209-page table row",
+            "commit_sequence": seq,
             "copy_slots_mb": nbytes / 1e6, "copy_slots_ms": med, "copy_slots_ms_p10_p90": [p10, p90],
             "copy_slots_gbs": nbytes / (med * 1e-3) / 1e9, "copy_slots_frac_hbm_peak": nbytes / (med * 1e-3) / 1e9 /
             HBM_PEAK_GBS, "rotate_rows_ms": rmed}

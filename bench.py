@@ -1,6 +1,7 @@
 """Benchmark of the paged K/V-cache path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,shared,fp8,commit] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads prefill,fp8prefill,shared,fp8,commit]
+                    [--no-cpu-baseline]
 
 Prints ONE JSON line.  The headline workload is the bf16 GQA decode (64
 sequences, lengths uniform in [512, 4096], 32 q / 8 kv heads of 128, 32-token
@@ -52,8 +53,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", default="prefill,shared,fp8,commit",
-                    help="secondary workloads to run: comma list of prefill, shared, fp8, commit (or none)")
+    ap.add_argument("--workloads", default="prefill,fp8prefill,shared,fp8,commit",
+                    help="secondary workloads to run: comma list of prefill, fp8prefill, shared, fp8, commit (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -238,6 +239,42 @@ def run_prefill(torch, pkv, W, flush):
             "gflop": flops / 1e9, "prefill_ms": med, "prefill_ms_p10_p90": [p10, p90], "tflops": tflops,
             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "scatter_ms": smed,
             "scatter_gbs": scat_bytes / (smed * 1e-3) / 1e9, "scatter_plus_prefill_ms": both}
+
+
+def run_fp8_prefill(torch, pkv, W, flush):
+    """The block-causal prefill's geometry over an fp8 e4m3fn K/V pool (scale
+    per page and kv head; every key resident), bf16 queries and output."""
+    case = W.make_fp8_prefill_case("fp8_prefill", 3, 1003, 1, 1568, [1560], [5120], 24, 24, 128, 32, 1560,
+                                   num_pool_pages=512)
+    pool = pkv.Pool(to_dev(case.pool.k, torch), to_dev(case.pool.v, torch), to_dev(case.pool.k_scale, torch),
+                    to_dev(case.pool.v_scale, torch))
+    qkv = to_dev(case.qkv, torch)
+    hq, hkv, d, s_q = case.num_q_heads, case.num_kv_heads, qkv.shape[-1], case.s_q
+    tables, n_ctx, seq = to_dev(case.tables, torch), to_dev(case.n_ctx, torch), to_dev(case.seq_len, torch)
+    out = torch.empty((1, s_q, hq, d), dtype=torch.bfloat16, device="cuda:0")
+    q = qkv[:, :, :hq]
+    ws = torch.empty(max(16, pkv.pkv_attn_prefill_workspace_bytes(1, s_q, hq, hkv, d, case.max_keys)),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def prefill():
+        pkv.pkv_attn_prefill_block_causal(pool, q, tables, n_ctx, seq, case.causal_block_size, case.max_keys,
+                                          case.sm_scale, out, None, ws)
+
+    try:
+        prefill()
+        torch.cuda.synchronize()
+    except pkv.PkvError as e:
+        return {"error": str(e)}
+    for _ in range(5):
+        prefill()
+    seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
+    flops = 4.0 * d * hq * sum(ctx + seq_len for _ in range(seq_len))
+    med, p10, p90 = time_events(torch, prefill, 30, flush)
+    tflops = flops / (med * 1e-3) / 1e12
+    return {"workload": "fp8 e4m3fn K/V block-causal prefill: 24 heads x 128, 1560 real queries (1568 rows) over "
+                        "5120 cached keys + own block, 32-token pages, bf16 MFMA on K/V widened in LDS",
+            "gflop": flops / 1e9, "prefill_ms": med, "prefill_ms_p10_p90": [p10, p90], "tflops": tflops,
+            "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS}
 
 
 def run_shared_prefix(torch, pkv, W, flush):
@@ -484,7 +521,9 @@ def main():
     }
     workloads = {}
     flush = Flusher(torch)
-    runners = {"prefill": ("block_causal_prefill", run_prefill), "shared": ("shared_prefix_decode", run_shared_prefix),
+    runners = {"prefill": ("block_causal_prefill", run_prefill),
+               "fp8prefill": ("fp8_block_causal_prefill", run_fp8_prefill),
+               "shared": ("shared_prefix_decode", run_shared_prefix),
                "fp8": ("long_fp8_decode", run_long_fp8), "commit": ("exact_window_commit", run_commit)}
     for name in [w.strip() for w in args.workloads.split(",") if w.strip() and w.strip() != "none"]:
         key, fn = runners[name]

@@ -321,14 +321,20 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   const int D = pool->head_dim;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
-  if (q_dtype != PKV_BF16 || pool->dtype != PKV_BF16 || out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
-  if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * 2) % 16 != 0 || !aligned(q, 16) ||
+  if (q_dtype != PKV_BF16 || pool->dtype == PKV_F32 || out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  const bool fp8 = pool->dtype == PKV_FP8_E4M3FN;
+  if (fp8 && (D != 128 || pool->page_size < 32)) return PKV_ERR_UNSUPPORTED;
+  if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * elem_bytes(pool->dtype)) % 16 != 0 ||
+      !aligned(q, 16) ||
       (q_tok_stride * 2) % 16 != 0 || (q_head_stride * 2) % 16 != 0 || !aligned(out, 16))
     return PKV_ERR_ALIGN;
 
   PrefillParams p;
   p.k_pool = pool->k;
   p.v_pool = pool->v;
+  p.k_scale = pool->k_scale;
+  p.v_scale = pool->v_scale;
+  p.kv_fp8 = fp8;
   p.q = static_cast<const uint16_t*>(q);
   p.table = block_table;
   p.n_ctx = n_ctx;

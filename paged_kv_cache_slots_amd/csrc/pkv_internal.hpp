@@ -88,6 +88,8 @@ struct MergeParams {
 struct PrefillParams {
   const void* k_pool;
   const void* v_pool;
+  const float* k_scale;       // fp8 pools: [num_pages, num_kv_heads]
+  const float* v_scale;
   const uint16_t* q;          // bf16
   const int32_t* table;
   const int32_t* n_ctx;
@@ -108,6 +110,7 @@ struct PrefillParams {
   int32_t causal_block_size;
   int32_t q_tiles;            // ceil(s_q / q tile rows)
   int32_t out_bf16;
+  int32_t kv_fp8;             // K/V e4m3fn (head_dim 128, page_size >= 32)
   float scale_log2;
 };
 

@@ -65,16 +65,23 @@ constexpr int kThreads = 512;      // 8 waves, two per SIMD
 constexpr int kTableCache = 1024;  // page ids cached in LDS
 constexpr int kSlotFloats = 4 * 65 * 64;   // partial state: [row block][64 outputs + lse][lane]
 
-template <int D>
+// LDS of one workgroup.  bf16 pools: the LDS-DMA writes the bf16 tiles the
+// MFMAs read, NST stages each of K and V.  fp8 pools: the LDS-DMA writes raw
+// fp8 tiles (NST stages each); each step converts the tiles it needs into one
+// bf16 K tile and one bf16 V tile, which the MFMAs read.
+template <int D, bool kFp8>
 struct PSmem {
-  static constexpr int ROWB = D * 2;              // bytes of one key row in LDS (no padding: XOR swizzle)
-  static constexpr int CH = D / 8;                // 16-byte chunks per row
-  static constexpr int TB = kKT * ROWB;           // bytes of one K or V tile
-  static constexpr int NST = 3;                   // pipeline stages of each of K and V
-  static constexpr int STAGES = 2 * NST * TB;    // K stages, then V stages
-  static constexpr int RPI = 1024 / ROWB;         // rows written by one LDS-DMA instruction (64 lanes x 16 B)
+  static constexpr int ROWB = D * 2;              // bytes of one bf16 key row in LDS (no padding: XOR swizzle)
+  static constexpr int TB = kKT * ROWB;           // bytes of one bf16 K or V tile
+  static constexpr int DROWB = kFp8 ? D : 2 * D;  // bytes of one key row as the LDS-DMA writes it
+  static constexpr int CH = DROWB / 16;           // 16-byte chunks per DMA row
+  static constexpr int DTB = kKT * DROWB;         // bytes of one DMA tile
+  static constexpr int NST = 3;                   // DMA pipeline stages of each of K and V
+  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? 2 * TB : 0);   // K stages, V stages, bf16 K and V
+  static constexpr int RPI = 1024 / DROWB;        // rows written by one LDS-DMA instruction (64 lanes x 16 B)
   static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
   static_assert(RPI * IPW == 8, "a wave writes 8 rows of each tile");
+  static_assert(!kFp8 || kKT * CH == kThreads, "one 16-byte fp8 chunk of each of K and V per thread");
   static constexpr int COMBINE = 4 * 66 * 64 * 4;   // key-half join: [row block][64 + 2 values][lane] floats
   static constexpr int BYTES = STAGES > COMBINE ? STAGES : COMBINE;
 };
@@ -236,13 +243,23 @@ __device__ __forceinline__ void store_rows(const PrefillParams& p, int b, int h,
 
 }  // namespace
 
-template <int D>
+// Scales of the cached pages of an fp8 pool (the scale of a (page, kv head)
+// multiplies every code of its rows): the score multiplier c * k_scale, and
+// log2 / reciprocal of v_scale, which is folded into the exponent of P and
+// taken back out of the row sum.  Scales below 2^-100 (zero included) count
+// as 2^-100: their rows then contribute nothing measurable instead of 0 * inf.
+struct ScaleCache {
+  float a, vlog, vinv;
+};
+
+template <int D, bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
-  using S = PSmem<D>;
+  using S = PSmem<D, kFp8>;
   constexpr int KSTEPS = D / 16;   // k-steps of QK^T
   constexpr int DB = D / 32;       // 32-dim output blocks
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::BYTES];
   __shared__ int32_t pages[kTableCache];
+  __shared__ ScaleCache scales[kFp8 ? kTableCache : 1];
   __shared__ int32_t tcum[kMaxTailUnits + 1];
 
   const int tid = threadIdx.x;
@@ -260,8 +277,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
   const int shift = p.page_shift;
   const int pmask = (1 << shift) - 1;
-  const int row_b = p.num_kv_heads * D * 2;            // bytes between key rows of a page
-  const int64_t page_stride_b = p.page_stride * 2;
+  constexpr int esz = kFp8 ? 1 : 2;                    // bytes of a pool element
+  const int row_b = p.num_kv_heads * D * esz;          // bytes between key rows of a page
+  const int64_t page_stride_b = p.page_stride * esz;
   const uint8_t* kpool_b = reinterpret_cast<const uint8_t*>(p.k_pool);
   const uint8_t* vpool_b = reinterpret_cast<const uint8_t*>(p.v_pool);
 
@@ -296,7 +314,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       const int last_page = (x.kmax - 1) >> shift;
       auto cache_pages = [&](int first) {
         __syncthreads();
-        for (int i = tid; i < kTableCache && first + i <= last_page; i += kThreads) pages[i] = trow[first + i];
+        for (int i = tid; i < kTableCache && first + i <= last_page; i += kThreads) {
+          const int pg = trow[first + i];
+          pages[i] = pg;
+          if constexpr (kFp8) {
+            const int64_t si = (int64_t)pg * p.num_kv_heads + x.g;
+            const float ks = fmaxf(p.k_scale[si], 0x1p-100f), vs = fmaxf(p.v_scale[si], 0x1p-100f);
+            scales[i] = ScaleCache{c * ks, fast_log2(vs), 1.0f / vs};
+          }
+        }
         page_base = first;
         __syncthreads();
       };
@@ -308,10 +334,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // and its P is 0); tiles past the segment issue zero-range loads that
       // only write zeros into a free stage, so every iteration has the same
       // loads in flight.
-      const int64_t head_off_b = (int64_t)x.g * D * 2;
-      const int rec_bytes = ((1 << shift) - 1) * row_b + D * 2;
-      auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::TB; };
-      auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::TB; };
+      const int64_t head_off_b = (int64_t)x.g * D * esz;
+      const int rec_bytes = ((1 << shift) - 1) * row_b + D * esz;
+      // DMA rings, and the tiles the MFMAs read (the same for bf16 pools)
+      auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::DTB; };
+      auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::DTB; };
+      auto kcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB : kstage(t); };
+      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB + S::TB : vstage(t); };
+      // fp8: widen one DMA tile into its bf16 tile (swizzled as the bf16 DMA
+      // would have written it); thread tid owns 16 codes: row tid / CH,
+      // columns 16 (tid % CH) .. + 15.  Codes convert exactly (scale 1).
+      auto widen = [&](const uint8_t* raw, uint8_t* bf, bool is_k) {
+        if constexpr (kFp8) {
+          const int r = tid / S::CH, cc = tid % S::CH;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(raw + r * S::DROWB + 16 * cc);
+          uint32_t h[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            h[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, false));
+            h[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, true));
+          }
+          const int sw = is_k ? swz_k<D>(r) : swz_v<D>(r);
+          uint8_t* row = bf + r * S::ROWB;
+          *reinterpret_cast<u32x4*>(row + (((2 * cc) ^ sw) << 4)) = u32x4{h[0], h[1], h[2], h[3]};
+          *reinterpret_cast<u32x4*>(row + (((2 * cc + 1) ^ sw) << 4)) = u32x4{h[4], h[5], h[6], h[7]};
+        }
+      };
+      // scales of this wave's key half of tile t (fp8; the half is one page).
+      // A half wholly past the unit's last key (all its scores masked) takes
+      // the last key's page, which is cached: its scale must be finite.
+      auto tile_scales = [&](int t) {
+        if constexpr (kFp8) return scales[(min(t * kKT + 32 * kh, x.kmax - 1) >> shift) - page_base];
+        return ScaleCache{c, 0.f, 1.f};
+      };
       auto dma_tile = [&](const uint8_t* pool_b, uint8_t* tile, int t, bool is_k) {
         const bool live = t < t1;
         const int kmax1 = x.kmax - 1;
@@ -323,13 +378,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           const int r0 = S::RPI * (wave * S::IPW + j);
           const int r = r0 + lane / S::CH;
           const int key = min(t * kKT + r, kmax1);
-          const int cc = (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
-          dma16(base, live ? rec_bytes : 0, tile + r0 * S::ROWB, (key & pmask) * row_b + cc * 16);
+          const int cc = kFp8 ? lane % S::CH : (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
+          dma16(base, live ? rec_bytes : 0, tile + r0 * S::DROWB, (key & pmask) * row_b + cc * 16);
         }
       };
       // S^T of this wave's key half of K tile t: keys 32 kh + 8 (i / 4) + 4 hf + (i % 4)
       auto qk = [&](int t, f32x16& acc) {
-        const uint8_t* kt = kstage(t);
+        const uint8_t* kt = kcomp(t);
         const int kr = 32 * kh + ln;
         u32x4 a[KSTEPS];
 #pragma unroll
@@ -344,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // group (hf, dh) reads rows 32 kh + 16 mu + 4 hf + 0..3 (and + 8) of dims
       // 32 d + 16 dh .. + 15, transposed.
       auto pv = [&](int t, const u32x4 (&pk)[2]) {
-        const uint8_t* vt = vstage(t);
+        const uint8_t* vt = vcomp(t);
         const int s16 = lane & 15;
         const int dh = (lane >> 4) & 1;
         u32x2 lo[2][DB], hi[2][DB];
@@ -399,6 +454,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       dma_tile(vpool_b, vstage(t0), t0, false);
       dma_tile(kpool_b, kstage(t0 + 2), t0 + 2, true);
       wait_dma_and_barrier<S::IPW>();
+      if constexpr (kFp8) {
+        widen(kstage(t0), kcomp(t0), true);
+        __syncthreads();
+      }
       f32x16 sA, sB;
       u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
       qk(t0, sA);
@@ -410,16 +469,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // s_cur / p_cur and s_next / p_prev trade roles between iterations.
       auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked) {
         // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight
+        if constexpr (kFp8) {
+          widen(kstage(t + 1), kcomp(t + 1), true);
+          asm volatile("" ::: "memory");   // one tile's temporaries at a time
+          widen(vstage(t - 1), vcomp(t - 1), false);
+          __syncthreads();
+        }
         if (need_refresh) {
           const int last_t = t + 3 < t1 ? t + 3 : t1 - 1;
-          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) cache_pages(((t + 1) * kKT) >> shift);
+          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) cache_pages((t * kKT) >> shift);
         }
         // refill: K(t+3) into K(t)'s stage, V(t+1) into V(t-2)'s stage
         dma_tile(kpool_b, kstage(t + 3), t + 3, true);
         dma_tile(vpool_b, vstage(t + 1), t + 1, false);
         // lazy rescale: the offset of a row moves only when its max grows by
         // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
-        const float mtc = mt * c;
+        const ScaleCache sct = tile_scales(t);   // tile t's page stays cached across a refresh
+        const float mtc = mt * sct.a;
         const bool grow = mtc > mc + 8.0f;
         if (__any(grow)) {
           const float mc_new = grow ? mtc : mc;
@@ -436,18 +502,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             }
           mc = mc_new;
         }
-        const float mcu = (mc == kNegInf) ? 0.f : mc;
+        // P of an fp8 tile carries the tile's V scale (exponent offset vlog);
+        // the row sum takes it back out
+        const float mcu = ((mc == kNegInf) ? 0.f : mc) - sct.vlog;
         float psum = 0.f;
 #pragma unroll
         for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            const float e0 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2], c, -mcu));
-            const float e1 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2 + 1], c, -mcu));
+            const float e0 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2], sct.a, -mcu));
+            const float e1 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2 + 1], sct.a, -mcu));
             psum += e0 + e1;
             p_cur[mu][q2] = pack_bf16x2(e0, e1);
           }
-        l += psum;
+        if constexpr (kFp8) l = fmaf(psum, sct.vinv, l);
+        else l += psum;
         qk(t + 1, s_next);
         pv(t - 1, p_prev);
         mt = mask_max(s_next, t + 1, masked);
@@ -476,6 +545,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       }
       // PV of the last tile (its P is in pB), then drain the trailing
       // zero-range loads before the stages are reused
+      if constexpr (kFp8) {
+        widen(vstage(t1 - 1), vcomp(t1 - 1), false);
+        __syncthreads();
+      }
       pv(t1 - 1, pB);
       wait_dma_and_barrier<0>();
     }
@@ -649,10 +722,12 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
   int g = sm_count > 0 ? sm_count : 8;
   if (g > kMaxPrefillWorkgroups) g = kMaxPrefillWorkgroups;
   g = g < 8 ? 8 : (g / 8) * 8;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+  if (p.kv_fp8)
+    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ws_o == nullptr) return e;
   // merge only when some XCD splits its leftover units (the same test as the kernels')

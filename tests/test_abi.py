@@ -101,6 +101,12 @@ def test_prefill_argument_checks():
     assert call(_pool(dtype=pkv.PKV_F32)) == 4
     assert call(p, qt=72 * 128 + 1) == 6
     assert call(p, s_q=0) == 0
+    # fp8 K/V: scales required; head_dim 128 and pages of >= 32 tokens only
+    assert call(_pool(dtype=pkv.PKV_FP8_E4M3FN)) == 1
+    fp8 = dict(dtype=pkv.PKV_FP8_E4M3FN, k_scale=3 * A, v_scale=4 * A)
+    assert call(_pool(page_size=16, page_stride=16 * 8 * 128, **fp8), maxk=4096) == 4
+    assert call(_pool(head_dim=64, page_stride=32 * 8 * 64, **fp8)) == 4
+    assert call(_pool(page_stride=32 * 8 * 128 + 8, **fp8)) == 6
 
 
 def test_merge_argument_checks():

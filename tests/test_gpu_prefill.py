@@ -155,3 +155,75 @@ def test_prefill_many_units_stream_k():
     c = W.make_prefill_case("many_units", 95, 1095, 2, 700, [650, 333], [1200, 77], 16, 4, 128, 32, 100,
                             extra_table_cols=1)
     check(c, rows=[(0, i) for i in (0, 99, 100, 255, 256, 649, 650, 699)] + [(1, i) for i in (0, 200, 332, 333)])
+
+
+# --------------------------------------------------------------------------- fp8 K/V pools
+
+def run_fp8_prefill(c, use_ws=True, out_dtype=torch.bfloat16):
+    pool = pool_to_dev(c.pool)
+    qkv = to_dev(c.qkv)
+    b, s_q, _, d = qkv.shape
+    hq, hkv = c.num_q_heads, c.num_kv_heads
+    ws = None
+    if use_ws:
+        nb = pkv.pkv_attn_prefill_workspace_bytes(b, s_q, hq, hkv, d, c.max_keys)
+        ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = torch.full((b, s_q, hq, d), float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full((b, s_q, hq), float("nan"), dtype=torch.float32, device=DEV)
+    pkv.pkv_attn_prefill_block_causal(pool, qkv[:, :, :hq], to_dev(c.tables), to_dev(c.n_ctx), to_dev(c.seq_len),
+                                      c.causal_block_size, c.max_keys, c.sm_scale, out, lse, ws)
+    torch.cuda.synchronize()
+    return as_f64(from_dev(out)), from_dev(lse).astype(np.float64)
+
+
+def check_fp8(c, rows=None, use_ws=True, out_dtype=torch.bfloat16):
+    note(f"prefill fp8 {c.name} B={c.qkv.shape[0]} s_q={c.s_q} seq={list(c.seq_len)} n_ctx={list(c.n_ctx)} "
+         f"Hq={c.num_q_heads} Hkv={c.num_kv_heads} ps={c.pool.page_size} cbs={c.causal_block_size} ws={use_ws}")
+    got, got_lse = run_fp8_prefill(c, use_ws, out_dtype)
+    ref, ref_lse = orc.attn_prefill_block_causal(c.pool.k, c.pool.v, c.qkv[:, :, :c.num_q_heads], c.tables, c.n_ctx,
+                                                 c.seq_len, c.causal_block_size, c.sm_scale, kv_dtype="fp8",
+                                                 q_dtype="bf16", k_scale=c.pool.k_scale, v_scale=c.pool.v_scale,
+                                                 rows_subset=rows)
+    if rows is not None:
+        bi, ii = np.array([x[0] for x in rows]), np.array([x[1] for x in rows])
+        got, got_lse, ref, ref_lse = got[bi, ii], got_lse[bi, ii], ref[bi, ii], ref_lse[bi, ii]
+    assert not np.any(np.isnan(got))
+    err = assert_close(got, ref, "fp8", f"{c.name} out")
+    assert_close(got_lse, ref_lse, "fp8", f"{c.name} lse")
+    print(f"[fp8 prefill] {c.name}: max |out - oracle| = {err:.3g}")
+
+
+FP8 = [
+    # name, B, s_q, seq_lens, n_ctx, Hq, Hkv, D, ps, cbs, zero-scale pages
+    ("fp8_one_block", 1, 200, [200], [300], 4, 4, 128, 32, 0, 0),
+    ("fp8_padded_gqa", 2, 150, [131, 150], [64, 5], 8, 2, 128, 32, 0, 0),
+    ("fp8_blocks_of_37_ps64", 1, 260, [250], [97], 2, 2, 128, 64, 37, 0),
+    ("fp8_no_context_zero_scales", 1, 129, [129], [0], 3, 3, 128, 32, 100, 2),
+    ("fp8_all_padding_batch", 2, 40, [0, 33], [12, 40], 2, 2, 128, 32, 8, 0),
+]
+
+
+@pytest.mark.parametrize("use_ws", [True, False], ids=["stream_k", "per_unit"])
+@pytest.mark.parametrize("case", FP8, ids=[s[0] for s in FP8])
+def test_prefill_fp8_small_exhaustive(case, use_ws):
+    name, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs, zeros = case
+    c = W.make_fp8_prefill_case(name, 96, 1096, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs,
+                                num_pool_pages=sum(math.ceil((s + x) / ps) for s, x in zip(seqs, ctxs)) + 5,
+                                extra_table_cols=2, zero_scale_pages=zeros)
+    check_fp8(c, use_ws=use_ws)
+
+
+def test_prefill_fp8_long_context_refreshes_page_cache():
+    """More pages than the kernel caches at once (1024): page ids and scales
+    are re-read part-way along the keys."""
+    c = W.make_fp8_prefill_case("fp8_long", 97, 1097, 1, 64, [64], [40000], 2, 1, 128, 32, 0)
+    check_fp8(c, out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("use_ws", [True, False], ids=["stream_k", "per_unit"])
+def test_prefill_fp8_full_size_sampled(use_ws):
+    """The block-causal workload's geometry (24 heads, 5120 cached keys, 1560
+    queries in 1568 rows, one causal block) over an fp8 pool."""
+    c = W.make_fp8_prefill_case("fp8_full", 98, 1098, 1, 1568, [1560], [5120], 24, 24, 128, 32, 1560)
+    rows = sorted({(0, i) for i in [0, 1, 127, 128, 779, 1000, 1535, 1536, 1559, 1560, 1567]})
+    check_fp8(c, rows=rows, use_ws=use_ws)

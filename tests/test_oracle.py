@@ -613,3 +613,33 @@ def test_causal_layout_rejects_what_it_cannot_lay_out():
                    dict(table=case["table"][:4]), dict(block_sizes=[2, 13])):
         with pytest.raises(ValueError):
             orc.causal_layout(**{**args, **change})
+
+
+def test_fp8_prefill_equals_prefill_over_torch_dequantised_pool():
+    """An e4m3fn pool with a scale per (page, kv head) attends exactly like an
+    fp32 pool holding torch's dequantisation code -> f32 x scale."""
+    rng = np.random.default_rng(21)
+    n_pages, ps, hkv, d = 9, 16, 2, 32
+    codes_k = rng.integers(0, 256, size=(n_pages, ps, hkv, d), dtype=np.uint8)
+    codes_v = rng.integers(0, 256, size=(n_pages, ps, hkv, d), dtype=np.uint8)
+    for c in (codes_k, codes_v):                         # no NaN codes (0x7F, 0xFF)
+        c[(c & 0x7F) == 0x7F] = 0x3C
+    # power-of-two scales: code x scale is exact in float32, so both pools hold
+    # the same values; a wrong page or head of a scale still changes them
+    ks = np.exp2(rng.integers(-9, -2, size=(n_pages, hkv))).astype(np.float32)
+    vs = np.exp2(rng.integers(-9, -2, size=(n_pages, hkv))).astype(np.float32)
+
+    def deq(codes, sc):
+        f = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+        return (f * torch.from_numpy(sc)[:, None, :, None]).numpy()
+
+    tables = np.array([[4, 1, 7, 0, 2, 8]], dtype=np.int32)
+    q = rng.standard_normal((1, 40, 4, d)).astype(np.float32)
+    qb = torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    n_ctx, seq = np.array([50], np.int32), np.array([37], np.int32)
+    a, la = orc.attn_prefill_block_causal(codes_k, codes_v, qb, tables, n_ctx, seq, 10, 0.2, kv_dtype="fp8",
+                                          q_dtype="bf16", k_scale=ks, v_scale=vs)
+    b, lb = orc.attn_prefill_block_causal(deq(codes_k, ks), deq(codes_v, vs), qb, tables, n_ctx, seq, 10, 0.2,
+                                          kv_dtype="f32", q_dtype="bf16")
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=1e-12, atol=1e-12)

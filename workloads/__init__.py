@@ -424,6 +424,38 @@ def make_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, num_q
                        poison_page)
 
 
+def make_fp8_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, num_q_heads, num_kv_heads,
+                          head_dim, page_size, causal_block_size, num_pool_pages=None, extra_table_cols=1,
+                          zero_scale_pages=0):
+    """Prefill over an fp8 e4m3fn K/V pool: every key, the current block's
+    included, is resident (quantised with a scale per (page, kv head)); Q is
+    bf16, rows ``seq_len[b] ..`` are padding; dead rows of the last page are
+    NaN codes.  ``zero_scale_pages`` owned pages get K and V scales of 0."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    n_ctxs = np.asarray(n_ctxs, dtype=np.int64)
+    totals = n_ctxs + seq_lens
+    pages_per_seq = [math.ceil(int(t) / page_size) for t in totals]
+    if num_pool_pages is None:
+        num_pool_pages = int(sum(pages_per_seq)) + 1
+    page_lists, poison_page, _ = _assign_pages(perm_seed, num_pool_pages, pages_per_seq)
+    tables = _table(page_lists, max(pages_per_seq) + extra_table_cols, poison_page)
+    owned = np.concatenate(page_lists)
+    valid = []
+    for t, pages in zip(totals, page_lists):
+        valid += [max(0, min(page_size, int(t) - j * page_size)) for j in range(len(pages))]
+    pool = _fill_pool(seed, num_pool_pages, page_size, num_kv_heads, head_dim, "fp8", owned, valid)
+    if zero_scale_pages:
+        pick = np.random.Generator(np.random.PCG64(seed + 11)).choice(owned, zero_scale_pages, replace=False)
+        pool.k_scale[pick] = 0.0
+        pool.v_scale[pick] = 0.0
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    qkv_f = rng.standard_normal((batch, s_q, num_q_heads + 2 * num_kv_heads, head_dim), dtype=np.float32)
+    slots = np.full(batch * s_q, -1, dtype=np.int64)
+    return PrefillCase(name, pool, to_storage(qkv_f, "bf16"), num_q_heads, num_kv_heads, tables,
+                       n_ctxs.astype(np.int32), seq_lens.astype(np.int32), causal_block_size,
+                       1.0 / math.sqrt(head_dim), slots, poison_page)
+
+
 def block_causal_prefill(seed=3, causal_block_size=1560):
     """bf16 block-causal prefill (video-generation style): 24 heads of 128,
     32-token pages, pinned prefix 1024 + rolling history 4096 + a current block

@@ -167,6 +167,30 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_attn_decode_step -- paged decode of a multi-token step (speculative
+ * verification: draft tokens + 1 per row).
+ * [P5] commit on the n-sample path with CUDA graphs (one kernel serves up to
+ * 16 query tokens per row, the verification steps of K draft tokens + 1) and
+ * the FA4 tail commit (the step's K/V is written into the row's pages first,
+ * then attended causally).
+ *
+ * As pkv_attn_decode with rows_per_table = q_len, except that the q_len rows
+ * of table row t are the tokens of one step, already written as the last
+ * q_len keys of the row: row j (0 <= j < q_len) attends logical keys
+ * [0, kv_lens[t] - (q_len - 1 - j)).  A row left with no key (kv_lens[t] <
+ * q_len - j) gets out = 0 and lse = -inf.  The workspace size is
+ * pkv_attn_decode_workspace_bytes(num_tables, q_len, ...).  q_len >= 1 (the
+ * pages' kernels serve up to 16; any count works here).
+ * Errors: as pkv_attn_decode.
+ */
+pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                int32_t num_tables, int32_t q_len, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t table_stride, const int32_t* kv_lens,
+                                int32_t max_kv_len, float sm_scale,
+                                void* out, pkv_dtype out_dtype, float* out_lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pkv_attn_prefill_block_causal -- paged prefill with causal blocks.
  * [P1] Description / Cache (frame-causal attention needs no mask: the new
  * tokens are cut into causal blocks, each with its own key count, full

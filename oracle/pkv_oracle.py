@@ -235,6 +235,39 @@ def attn_decode(k_pool, v_pool, q, tables, kv_lens, sm_scale, kv_dtype="bf16", q
     return out, lse
 
 
+def attn_decode_step(k_pool, v_pool, q, tables, kv_lens, sm_scale, kv_dtype="bf16", q_dtype=None,
+                     k_scale=None, v_scale=None):
+    """Paged decode of a multi-token step ([P5] n-sample commit with CUDA
+    graphs: up to 16 query tokens per row, the K draft tokens + 1 of a
+    verification step; FA4 tail commit: the step's K/V is in the row's pages
+    and is attended causally).
+
+    ``q`` is ``[T, n, Hq, D]``: the n tokens of row t are its last n keys, so
+    token j attends logical keys ``0 .. kv_lens[t] - (n - 1 - j) - 1`` (none,
+    giving ``o = 0`` and ``lse = -inf``, when that count is not positive).
+    Returns ``(out [T, n, Hq, D], lse [T, n, Hq])`` in float64.
+    """
+    if q_dtype is None:
+        q_dtype = "bf16" if kv_dtype == "fp8" else kv_dtype
+    qf = _decode(q, q_dtype)
+    n_t, n_rows, n_qh, head_dim = qf.shape
+    group = n_qh // k_pool.shape[2]
+    out = np.full((n_t, n_rows, n_qh, head_dim), np.nan)
+    lse = np.full((n_t, n_rows, n_qh), np.nan)
+    for t in range(n_t):
+        length = int(kv_lens[t])
+        keys = _gather_real(k_pool, tables[t], length, kv_dtype, k_scale)
+        vals = _gather_real(v_pool, tables[t], length, kv_dtype, v_scale)
+        for j in range(n_rows):
+            seen = max(0, length - (n_rows - 1 - j))
+            for h in range(n_qh):
+                o, s_ = attention_rows(qf[t, j:j + 1, h, :], keys[:seen, h // group, :], vals[:seen, h // group, :],
+                                       sm_scale)
+                out[t, j, h, :] = o[0]
+                lse[t, j, h] = s_[0]
+    return out, lse
+
+
 # ----------------------------------------------------------------------------
 # Block-causal paged prefill  [P1] Description / Cache and / Attention
 # ----------------------------------------------------------------------------

@@ -30,7 +30,7 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
 EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
             "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
-            "pkv_window_evicted_tokens", "pkv_causal_layout"]
+            "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step"]
 
 
 class PkvError(RuntimeError):
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_attn_decode_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_decode": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
                                            ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_decode_step": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
+                                                ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
                                                          P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
@@ -169,6 +171,23 @@ def pkv_attn_decode(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_l
     ps = pool.struct()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pkv_attn_decode", load_library().pkv_attn_decode(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
+        block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
+        _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_decode_step(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor,
+                         max_kv_len: int, sm_scale: float, out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode of a multi-token step.  ``q`` is [T, q_len, Hq, D] contiguous:
+    the q_len tokens of row t are its last q_len keys, token j attending keys
+    [0, kv_lens[t] - (q_len - 1 - j)).  ``out`` / ``out_lse`` as pkv_attn_decode."""
+    if not q.is_contiguous() or not out.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q, out and block_table must be contiguous")
+    t, n, hq, _ = q.shape
+    ps = pool.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attn_decode_step", load_library().pkv_attn_decode_step(
         ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
         block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
         _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -151,7 +151,7 @@ struct RowState {
 
 template <int D, bool kFp8>
 __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>& r, const u32x4 (&q)[D / 32],
-                                             float scale_log2, int key0, int len) {
+                                             float scale_log2, int key0, int len, int lim, int lim_lo) {
   using T = TileRegs<D, kFp8>;
   constexpr int NCH = T::NCH;
   constexpr int DPL = D / 16;
@@ -184,18 +184,19 @@ __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>&
     }
     s[h] = acc;
   }
-  // ---- scale (and fp8 K scale), mask keys past the end
+  // ---- scale (and fp8 K scale), mask keys at or past the lane's row limit
+  // (lim; lim_lo <= every row's limit is wave-uniform)
   const float c0 = kFp8 ? scale_log2 * r.ks0 : scale_log2;
   const float c1 = kFp8 ? scale_log2 * r.ks1 : scale_log2;
   s[0] *= c0;
   s[1] *= c1;
-  const bool partial = key0 + 32 > len;
+  const bool partial = key0 + 32 > lim_lo;
   if (partial) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (key0 + 16 * h + 4 * j + i >= len) s[h][i] = kNegInf;
+        if (key0 + 16 * h + 4 * j + i >= lim) s[h][i] = kNegInf;
   }
   // ---- online softmax (row max shared by the 4 lanes of a row)
   float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -233,9 +234,10 @@ __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>&
   pb[3] = pack_bf16x2(pv[6], pv[7]);
 
   // ---- V^T operands (8 keys of this lane group, one dim each); dead keys of
-  // a partial tile are zeroed in place first (0 * NaN would poison the sum)
+  // a tile past the row's last key are zeroed in place first (0 * NaN would
+  // poison the sum).  Keys a causal row only masks are real and stay.
   constexpr int VW = T::VB / 4 > 0 ? T::VB / 4 : 1;   // raw dwords per key
-  if (partial) {
+  if (key0 + 32 > len) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const bool ok = key0 + 16 * (t >> 2) + 4 * j + (t & 3) < len;
@@ -305,7 +307,8 @@ __device__ __forceinline__ void reset_state(RowState<D>& st) {
 // unconditional loads (zero-range descriptor past the window's end).
 template <int D, bool kFp8>
 __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
-                                           const int32_t* trow, int g, int len, int first, int step, int n) {
+                                           const int32_t* trow, int g, int len, int lim, int lim_lo, int first,
+                                           int step, int n) {
   constexpr int esz = kFp8 ? 1 : 2;
   const int lane = threadIdx.x & 63;
   const int r_lane = lane & 15, j = lane >> 4;
@@ -338,10 +341,10 @@ __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D /
     issue(A, 0);
     for (int k = 0; k < n_win; k += 2) {
       issue(B, k + 1);
-      compute_tile<D, kFp8>(st, A, q, p.scale_log2, (first + (w0 + k) * step) * 32, len);
+      compute_tile<D, kFp8>(st, A, q, p.scale_log2, (first + (w0 + k) * step) * 32, len, lim, lim_lo);
       if (k + 1 >= n_win) break;
       issue(A, k + 2);
-      compute_tile<D, kFp8>(st, B, q, p.scale_log2, (first + (w0 + k + 1) * step) * 32, len);
+      compute_tile<D, kFp8>(st, B, q, p.scale_log2, (first + (w0 + k + 1) * step) * 32, len, lim, lim_lo);
     }
   }
 }
@@ -378,6 +381,12 @@ __device__ __forceinline__ void row_of(const DecodeParams& p, int t, int g, int 
   qi = r / p.group;
   const int qh = g * p.group + (r - qi * p.group);
   qrow = ((int64_t)t * p.rows_per_table + qi) * p.num_q_heads + qh;
+}
+
+// Keys row qi of a table row with len keys sees: all of them, or for a step
+// of n causal tokens (the last n keys of the row) the keys up to its own.
+__device__ __forceinline__ int row_limit(const DecodeParams& p, int len, int qi) {
+  return p.causal ? len - (p.rows_per_table - 1 - qi) : len;
 }
 
 }  // namespace
@@ -421,7 +430,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   const int first = tb + wp;
   const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
   if (rb * 16 < R && n_mine > 0)
-    walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, first, WP, n_mine);
+    walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                        row_limit(p, len, 0), first, WP, n_mine);
 
   st.l += __shfl_xor(st.l, 16, 64);
   st.l += __shfl_xor(st.l, 32, 64);
@@ -559,7 +569,8 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
     reset_state(st);
     const int len = p.kv_lens[t];
     if (rb * 16 < R)
-      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, k0, 1, k1 - k0);
+      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                          row_limit(p, len, 0), k0, 1, k1 - k0);
     st.l += __shfl_xor(st.l, 16, 64);
     st.l += __shfl_xor(st.l, 32, 64);
     const bool empty = st.l == 0.f;
@@ -692,7 +703,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   te = te < tiles ? te : tiles;
   if (p.splits > 1 && tb >= te) return;
   const int kb = tb * 32;
-  const int ke = min(te * 32, len);
+  const int qi = (int)((qrow / p.num_q_heads) % p.rows_per_table);
+  const int ke = min(te * 32, row_limit(p, len, qi));
 
   __shared__ float qs[D];
   for (int d = lane; d < D; d += 64) {

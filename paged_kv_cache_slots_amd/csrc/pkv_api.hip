@@ -187,11 +187,13 @@ size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_tabl
   return split > sk ? split : sk;
 }
 
-pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
-                           int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
-                           int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
-                           void* out, pkv_dtype out_dtype, float* out_lse, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+// Decode of num_tables x rows_per_table query rows; with `causal` the rows of
+// a table row are the tokens of one step (row i sees len - (n - 1 - i) keys).
+static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
+                              int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
+                              int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                              void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
+                              size_t workspace_bytes, int32_t causal, hipStream_t stream) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
@@ -268,6 +270,7 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   p.out_bf16 = out_dtype == PKV_BF16;
   p.n_workers = 0;
   p.row_groups = sk_rg;
+  p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
 
   if (use_sk) return launch_decode_sk(p, elem_type(pool->dtype), D, cus, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -293,6 +296,24 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
   return PKV_OK;
 }
 
+
+pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
+                           int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
+                           int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                           void* out, pkv_dtype out_dtype, float* out_lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return decode_call(pool, q, q_dtype, num_tables, rows_per_table, num_q_heads, block_table, table_stride, kv_lens,
+                     max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 0, stream);
+}
+
+pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
+                                int32_t q_len, int32_t num_q_heads, const int32_t* block_table,
+                                int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                                void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(pool, q, q_dtype, num_tables, q_len, num_q_heads, block_table, table_stride, kv_lens,
+                     max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 1, stream);
+}
 // ---------------------------------------------------------------------------
 size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_keys) {

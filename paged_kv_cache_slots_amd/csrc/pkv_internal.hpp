@@ -67,6 +67,7 @@ struct DecodeParams {
   int32_t out_bf16;
   int32_t n_workers;          // stream-K workers (set by the launcher)
   int32_t row_groups;         // stream-K: row groups per (table row, kv head)
+  int32_t causal;             // rows of a table row are a step's tokens: row i sees len - (n - 1 - i) keys
   float scale_log2;           // sm_scale * log2(e)
 };
 

@@ -643,3 +643,49 @@ def test_fp8_prefill_equals_prefill_over_torch_dequantised_pool():
                                           kv_dtype="f32", q_dtype="bf16")
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(la, lb, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- multi-token decode step
+
+def test_decode_step_matches_masked_sdpa_and_empty_rows():
+    """Token j of an n-token step attends keys [0, len - (n - 1 - j)): torch
+    SDPA with that boolean mask (GQA by repeating kv heads); rows left with no
+    key give 0 and -inf."""
+    rng = np.random.default_rng(31)
+    n_pages, ps, hkv, hq, d, n = 12, 16, 2, 4, 32, 5
+    kpool = rng.standard_normal((n_pages, ps, hkv, d)).astype(np.float32)
+    vpool = rng.standard_normal((n_pages, ps, hkv, d)).astype(np.float32)
+    tables = np.array([[3, 7, 1, 0], [5, 9, 2, 11], [4, 6, 8, 10]], dtype=np.int32)
+    lens = np.array([41, 3, 64], dtype=np.int32)          # row 1: fewer keys than step tokens
+    q = rng.standard_normal((3, n, hq, d)).astype(np.float32)
+    out, lse = orc.attn_decode_step(kpool, vpool, q, tables, lens, 0.3, kv_dtype="f32")
+    for t in range(3):
+        L = int(lens[t])
+        k = np.concatenate([kpool[p] for p in tables[t]])[:L]        # [L, hkv, d]
+        v = np.concatenate([vpool[p] for p in tables[t]])[:L]
+        kt = torch.from_numpy(np.repeat(k, hq // hkv, axis=1)).permute(1, 0, 2).double()   # [hq, L, d]
+        vt = torch.from_numpy(np.repeat(v, hq // hkv, axis=1)).permute(1, 0, 2).double()
+        qt = torch.from_numpy(q[t]).permute(1, 0, 2).double()                             # [hq, n, d]
+        lim = np.array([L - (n - 1 - j) for j in range(n)])
+        mask = torch.from_numpy(np.arange(L)[None, :] < lim[:, None])                   # [n, L]
+        live = lim > 0
+        if live.any():
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.3)
+            scores = (qt @ kt.transpose(1, 2)) * 0.3
+            ref_lse = torch.logsumexp(scores.masked_fill(~mask, float("-inf")), dim=-1)
+            np.testing.assert_allclose(out[t][live], ref.permute(1, 0, 2).numpy()[live], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[t][live], ref_lse.permute(1, 0).numpy()[live], rtol=1e-12, atol=1e-12)
+        assert np.all(out[t][~live] == 0) and np.all(np.isneginf(lse[t][~live]))
+    assert (~(np.array([int(lens[1]) - (n - 1 - j) for j in range(n)]) > 0)).sum() == 2
+
+
+def test_decode_step_of_one_token_is_plain_decode():
+    rng = np.random.default_rng(32)
+    kpool = rng.standard_normal((6, 16, 1, 32)).astype(np.float32)
+    vpool = rng.standard_normal((6, 16, 1, 32)).astype(np.float32)
+    tables = np.array([[2, 0, 5], [1, 3, 4]], dtype=np.int32)
+    lens = np.array([40, 17], dtype=np.int32)
+    q = rng.standard_normal((2, 1, 2, 32)).astype(np.float32)
+    a = orc.attn_decode_step(kpool, vpool, q, tables, lens, 0.2, kv_dtype="f32")
+    b = orc.attn_decode(kpool, vpool, q, tables, lens, 0.2, kv_dtype="f32")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

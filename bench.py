@@ -311,11 +311,21 @@ def run_shared_prefix(torch, pkv, W, flush):
         pkv.pkv_scatter_slots(pool, new_k, new_v, slots)
         pkv.pkv_attn_decode(pool, q, ft, flen, mf, c.sm_scale, uout, None, ws2)
 
+    fout = torch.empty((n_rows, 1, hq, d), dtype=torch.bfloat16, device="cuda:0")
+    ws3 = torch.empty(pkv.pkv_attn_decode_shared_prefix_workspace_bytes(g, s, 1, hq, d, mp), dtype=torch.uint8,
+                      device="cuda:0")
+
+    def fused():
+        pkv.pkv_scatter_slots(pool, new_k, new_v, slots)
+        pkv.pkv_attn_decode_shared_prefix(pool, q, s, pt, plen, mp, tt, tlen, mt, c.sm_scale, fout, ws3)
+
     for _ in range(5):
         shared()
         unshared()
+        fused()
     med, p10, p90 = time_events(torch, shared, 30, flush)
     umed, _, _ = time_events(torch, unshared, 30, flush)
+    fmed, fp10, fp90 = time_events(torch, fused, 30, flush)
     pre = decode_bytes(c.prefix_lens, 32, hkv, d, 2, n_rows, hq, 2, 4, True, False)
     tail = decode_bytes(c.tail_lens, 32, hkv, d, 2, n_rows, hq, 2, 4, True, False)
     merge = 2 * n_rows * hq * (d + 1) * 4 + n_rows * hq * d * 2
@@ -325,7 +335,10 @@ def run_shared_prefix(torch, pkv, W, flush):
     return {"workload": "shared-prefix n-sample decode: 8 prompts x 16 samples, 2048-token shared prefix, tails "
                         "U[1,512], 32/8 heads x 128, bf16 (scatter + prefix decode + tail decode + merge)",
             "algorithmic_mb": total / 1e6, "step_ms": med, "step_ms_p10_p90": [p10, p90], "gbs": gbs,
-            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "unshared_step_ms": umed,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "fused_step_ms": fmed, "fused_step_ms_p10_p90": [fp10, fp90],
+            "fused_gbs": total / (fmed * 1e-3) / 1e9, "fused_frac_hbm_peak": total / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "fused_launches": 3, "unfused_launches": 6, "unshared_step_ms": umed,
             "unshared_mb": (decode_bytes(c.full_lens, 32, hkv, d, 2, n_rows, hq, 2, 2, False, False) + scat) / 1e6}
 
 

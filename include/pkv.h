@@ -191,6 +191,49 @@ pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_attn_decode_shared_prefix -- one n-sample decode step: shared prefix,
+ * private tails and their merge.
+ * [P5] commits on the n-sample path (rows whose tables start with the same
+ * pages form a group whose shared pages are read once and merged with every
+ * row's private tail; one fused kernel does prefix, tail and merge for up to
+ * 16 query tokens per row) and the FA4 tail and split commits (the step's
+ * tokens are attended causally in the tail; prefix and tail states are joined
+ * in natural-log LSE; an empty run has LSE -inf).
+ *
+ *   q             [groups * samples, q_len, num_q_heads, head_dim] bf16,
+ *                 contiguous; sample r belongs to group r / samples.
+ *   prefix_table  device int32 [groups, prefix_stride], prefix_lens device
+ *                 int32 [groups] (<= max_prefix_len): the group's shared keys.
+ *   tail_table    device int32 [groups * samples, tail_stride], tail_lens
+ *                 device int32 [groups * samples] (<= max_tail_len): the
+ *                 sample's private keys, its step's q_len tokens last.
+ *   out, out_lse  as pkv_attn_decode for q's shape.
+ * Query token j of sample r attends prefix keys [0, prefix_lens[g]) and tail
+ * keys [0, tail_lens[r] - (q_len - 1 - j)) (none when that is not positive).
+ *   workspace     device scratch of at least
+ *                 pkv_attn_decode_shared_prefix_workspace_bytes(...) bytes,
+ *                 16-byte aligned, contents ignored: the fp32 states of the
+ *                 prefix's key splits (>= 512 keys each, <= 16) and of the
+ *                 tails.  Two calls in flight need two workspaces.
+ * Kernels: one launch of every prefix-split and tail workgroup (bf16 MFMA;
+ * K/V bf16 or fp8 e4m3fn; head_dim 64 or 128; page_size >= 16), then one
+ * merge launch.
+ * Errors: as pkv_attn_decode; a missing or small workspace -> PKV_ERR_NULL /
+ * PKV_ERR_SHAPE; q not bf16 or an fp32 pool -> PKV_ERR_UNSUPPORTED.
+ */
+size_t pkv_attn_decode_shared_prefix_workspace_bytes(int32_t groups, int32_t samples, int32_t q_len,
+                                                     int32_t num_q_heads, int32_t head_dim, int32_t max_prefix_len);
+
+pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t groups,
+                                         int32_t samples, int32_t q_len, int32_t num_q_heads,
+                                         const int32_t* prefix_table, int32_t prefix_stride,
+                                         const int32_t* prefix_lens, int32_t max_prefix_len,
+                                         const int32_t* tail_table, int32_t tail_stride, const int32_t* tail_lens,
+                                         int32_t max_tail_len, float sm_scale, void* out, pkv_dtype out_dtype,
+                                         float* out_lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * pkv_attn_prefill_block_causal -- paged prefill with causal blocks.
  * [P1] Description / Cache (frame-causal attention needs no mask: the new
  * tokens are cut into causal blocks, each with its own key count, full

@@ -11,6 +11,7 @@ from .pkv_oracle import (  # noqa: F401
     E4M3FN_MAX,
     attention_rows,
     attn_decode,
+    attn_decode_shared_prefix,
     attn_decode_step,
     attn_prefill_block_causal,
     causal_layout,

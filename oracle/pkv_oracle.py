@@ -268,6 +268,43 @@ def attn_decode_step(k_pool, v_pool, q, tables, kv_lens, sm_scale, kv_dtype="bf1
     return out, lse
 
 
+def attn_decode_shared_prefix(k_pool, v_pool, q, samples, prefix_tables, prefix_lens, tail_tables, tail_lens,
+                              sm_scale, kv_dtype="bf16", q_dtype=None, k_scale=None, v_scale=None):
+    """One n-sample decode step ([P5] n-sample commits: a group's shared
+    pages are read once and merged with each row's private tail, for up to 16
+    query tokens per row; FA4 tail commit: the step's tokens are attended
+    causally in the tail).
+
+    ``q`` is ``[G * samples, n, Hq, D]``; token j of sample r attends the
+    ``prefix_lens[r // samples]`` keys of its group's prefix table followed by
+    the first ``tail_lens[r] - (n - 1 - j)`` keys of its tail table.
+    Returns ``(out [G * samples, n, Hq, D], lse [G * samples, n, Hq])`` float64.
+    """
+    if q_dtype is None:
+        q_dtype = "bf16" if kv_dtype == "fp8" else kv_dtype
+    qf = _decode(q, q_dtype)
+    n_r, n_tok, n_qh, head_dim = qf.shape
+    group = n_qh // k_pool.shape[2]
+    out = np.full((n_r, n_tok, n_qh, head_dim), np.nan)
+    lse = np.full((n_r, n_tok, n_qh), np.nan)
+    for r in range(n_r):
+        g = r // samples
+        pk = _gather_real(k_pool, prefix_tables[g], int(prefix_lens[g]), kv_dtype, k_scale)
+        pv = _gather_real(v_pool, prefix_tables[g], int(prefix_lens[g]), kv_dtype, v_scale)
+        tk = _gather_real(k_pool, tail_tables[r], int(tail_lens[r]), kv_dtype, k_scale)
+        tv = _gather_real(v_pool, tail_tables[r], int(tail_lens[r]), kv_dtype, v_scale)
+        for j in range(n_tok):
+            seen = max(0, int(tail_lens[r]) - (n_tok - 1 - j))
+            keys = np.concatenate([pk, tk[:seen]])
+            vals = np.concatenate([pv, tv[:seen]])
+            for h in range(n_qh):
+                o, s_ = attention_rows(qf[r, j:j + 1, h, :], keys[:, h // group, :], vals[:, h // group, :],
+                                       sm_scale)
+                out[r, j, h, :] = o[0]
+                lse[r, j, h] = s_[0]
+    return out, lse
+
+
 # ----------------------------------------------------------------------------
 # Block-causal paged prefill  [P1] Description / Cache and / Attention
 # ----------------------------------------------------------------------------

@@ -30,7 +30,8 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
 EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
             "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
-            "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step"]
+            "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
+            "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix"]
 
 
 class PkvError(RuntimeError):
@@ -73,6 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_decode_step": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
                                                 ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_decode_shared_prefix_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "pkv_attn_decode_shared_prefix": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, I32, P, I32, P, I32, P,
+                                                         I32, P, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
                                                          P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
@@ -191,6 +195,36 @@ def pkv_attn_decode_step(pool: Pool, q: torch.Tensor, block_table: torch.Tensor,
         ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
         block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
         _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_decode_shared_prefix_workspace_bytes(groups: int, samples: int, q_len: int, num_q_heads: int,
+                                                  head_dim: int, max_prefix_len: int) -> int:
+    return load_library().pkv_attn_decode_shared_prefix_workspace_bytes(groups, samples, q_len, num_q_heads, head_dim,
+                                                                         max_prefix_len)
+
+
+def pkv_attn_decode_shared_prefix(pool: Pool, q: torch.Tensor, samples: int, prefix_table: torch.Tensor,
+                                  prefix_lens: torch.Tensor, max_prefix_len: int, tail_table: torch.Tensor,
+                                  tail_lens: torch.Tensor, max_tail_len: int, sm_scale: float, out: torch.Tensor,
+                                  workspace: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                                  stream=None) -> None:
+    """One n-sample step: ``q`` [groups * samples, q_len, Hq, D] bf16; sample r
+    attends its group's prefix and its own tail, the step's q_len tokens being
+    the tail's last keys (causal among themselves)."""
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    if not prefix_table.is_contiguous() or not tail_table.is_contiguous():
+        raise ValueError("tables must be contiguous")
+    rows, q_len, hq, _ = q.shape
+    if rows % samples:
+        raise ValueError("q rows must be groups * samples")
+    ps = pool.struct()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("pkv_attn_decode_shared_prefix", load_library().pkv_attn_decode_shared_prefix(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), rows // samples, samples, q_len, hq,
+        prefix_table.data_ptr(), prefix_table.stride(0), prefix_lens.data_ptr(), int(max_prefix_len),
+        tail_table.data_ptr(), tail_table.stride(0), tail_lens.data_ptr(), int(max_tail_len), float(sm_scale),
+        out.data_ptr(), _dtype_code(out.dtype), _ptr(out_lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
 
 
 def pkv_attn_prefill_workspace_bytes(batch: int, s_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -395,15 +395,12 @@ __device__ __forceinline__ int row_limit(const DecodeParams& p, int len, int qi)
 // Split kernel: one workgroup per (key split, kv head, table row, row group).
 // Used without a stream-K workspace; with splits == 1 it needs no workspace.
 // ---------------------------------------------------------------------------
+// The work of one workgroup: key split s of (kv head g, table row t, row
+// group rg), WP waves per 16-row block.
 template <int D, bool kFp8, int WP>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g, int t, int rg) {
   constexpr int WR = 4 / WP;
   constexpr int DPL = D / 16;
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int n_rg = gridDim.z / p.num_tables;
-  const int t = blockIdx.z / n_rg;
-  const int rg = blockIdx.z - t * n_rg;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wr = wave / WP, wp = wave - (wave / WP) * WP;
   const int lane = threadIdx.x & 63;
@@ -416,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   const int tb = s * p.tiles_per_split;
   int te = tb + p.tiles_per_split;
   te = te < tiles ? te : tiles;
-  if (p.splits > 1 && tb >= te) return;   // empty split: the merge never reads it
+  if (p.splits > 1 && tb >= te && !p.write_state) return;   // empty split: the merge never reads it
 
   const int r = rb * 16 + r_lane;
   const bool row_ok = r < R;
@@ -473,13 +470,54 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
   const bool empty = st.l == 0.f;
   const float inv = empty ? 0.f : 1.0f / st.l;
   const float lse = empty ? kNegInf : (st.m + fast_log2(st.l)) * kLn2;
-  if (p.splits == 1) {
+  if (p.splits == 1 && !p.write_state) {
     store_row<D>(st, reinterpret_cast<uint8_t*>(p.out) + qrow * D * (p.out_bf16 ? 2 : 4), p.out_bf16, inv);
     if (p.out_lse && j == 0) p.out_lse[qrow] = lse;
   } else {
     const int64_t plane = (int64_t)p.num_tables * p.rows_per_table * p.num_q_heads;
     store_row<D>(st, p.ws_o + ((int64_t)s * plane + qrow) * D, false, inv);
     if (j == 0) p.ws_lse[(int64_t)s * plane + qrow] = lse;
+  }
+}
+
+// Split kernel: grid (split, kv head, table row x row group).
+template <int D, bool kFp8, int WP>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
+  const int n_rg = gridDim.z / p.num_tables;
+  const int t = blockIdx.z / n_rg;
+  decode_block<D, kFp8, WP>(p, blockIdx.x, blockIdx.y, t, blockIdx.z - t * n_rg);
+}
+
+// Row blocks of 16 rows and waves per row block for R rows (as the split
+// kernel's launcher chooses them).
+__host__ __device__ constexpr int waves_per_block(int R) { return R <= 16 ? 4 : (R <= 32 ? 2 : 1); }
+__host__ __device__ constexpr int row_groups_of(int R) { return R <= 32 ? 1 : ((R + 15) / 16 + 3) / 4; }
+
+// n-sample step, prefix + tail in one launch ("Support shared-prefix attention
+// for n-sample requests in FMHA": one kernel does the shared prefix, the
+// private tails and, with the merge kernel after it, their merge).  Blocks
+// [0, n_pre) are (prefix split, kv head, group, row group) work of `pre`: all
+// samples' step tokens of a group share each prefix K/V tile.  The others are
+// (tail, kv head, row group) work of `tail`, whose tokens are causal among
+// themselves.  Each leaves a normalised state; the state of query row x is at
+// row x of split s (prefix) or of split pre.splits (tail), so one N-state
+// merge finishes the step.
+template <int D, bool kFp8, int WPP, int WPT>
+__global__ __launch_bounds__(256, 2) void shared_prefix_kernel(DecodeParams pre, DecodeParams tail, int n_pre) {
+  const int b = blockIdx.x;
+  if (b < n_pre) {
+    const int s = b % pre.splits;
+    const int rest = b / pre.splits;
+    const int g = rest % pre.num_kv_heads;
+    const int z = rest / pre.num_kv_heads;
+    const int nrg = row_groups_of(pre.rows_per_table * pre.group);
+    decode_block<D, kFp8, WPP>(pre, s, g, z / nrg, z % nrg);
+  } else {
+    const int bt = b - n_pre;
+    const int g = bt % tail.num_kv_heads;
+    const int z = bt / tail.num_kv_heads;
+    const int nrg = row_groups_of(tail.rows_per_table * tail.group);
+    decode_block<D, kFp8, WPT>(tail, 0, g, z / nrg, z % nrg);
   }
 }
 
@@ -842,6 +880,39 @@ static hipError_t launch_sk_d(const DecodeParams& p, int sm_count, hipStream_t s
     case 2: return launch_sk_dw<D, kFp8, 2>(p, sm_count, stream);
     default: return launch_sk_dw<D, kFp8, 4>(p, sm_count, stream);
   }
+}
+
+template <int D, bool kFp8, int WPP>
+static hipError_t launch_shared_d(const DecodeParams& pre, const DecodeParams& tail, int n_pre, int n_all,
+                                  hipStream_t stream) {
+  const int wpt = waves_per_block(tail.rows_per_table * tail.group);
+  if (wpt == 4)
+    hipLaunchKernelGGL((shared_prefix_kernel<D, kFp8, WPP, 4>), dim3(n_all), dim3(256), 0, stream, pre, tail, n_pre);
+  else if (wpt == 2)
+    hipLaunchKernelGGL((shared_prefix_kernel<D, kFp8, WPP, 2>), dim3(n_all), dim3(256), 0, stream, pre, tail, n_pre);
+  else
+    hipLaunchKernelGGL((shared_prefix_kernel<D, kFp8, WPP, 1>), dim3(n_all), dim3(256), 0, stream, pre, tail, n_pre);
+  return hipGetLastError();
+}
+
+template <int D, bool kFp8>
+static hipError_t launch_shared_dk(const DecodeParams& pre, const DecodeParams& tail, hipStream_t stream) {
+  const int rp = pre.rows_per_table * pre.group, rt = tail.rows_per_table * tail.group;
+  const int64_t n_pre = (int64_t)pre.splits * pre.num_kv_heads * pre.num_tables * row_groups_of(rp);
+  const int64_t n_all = n_pre + (int64_t)tail.num_kv_heads * tail.num_tables * row_groups_of(rt);
+  if (n_all == 0) return hipSuccess;
+  const int wpp = waves_per_block(rp);
+  if (wpp == 4) return launch_shared_d<D, kFp8, 4>(pre, tail, (int)n_pre, (int)n_all, stream);
+  if (wpp == 2) return launch_shared_d<D, kFp8, 2>(pre, tail, (int)n_pre, (int)n_all, stream);
+  return launch_shared_d<D, kFp8, 1>(pre, tail, (int)n_pre, (int)n_all, stream);
+}
+
+hipError_t launch_shared_prefix(const DecodeParams& pre, const DecodeParams& tail, ElemType kv, int head_dim,
+                                hipStream_t stream) {
+  const bool fp8 = kv == kFP8;
+  if (head_dim == 128)
+    return fp8 ? launch_shared_dk<128, true>(pre, tail, stream) : launch_shared_dk<128, false>(pre, tail, stream);
+  return fp8 ? launch_shared_dk<64, true>(pre, tail, stream) : launch_shared_dk<64, false>(pre, tail, stream);
 }
 
 hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream) {

@@ -271,6 +271,7 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   p.n_workers = 0;
   p.row_groups = sk_rg;
   p.causal = causal;
+  p.write_state = 0;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
 
   if (use_sk) return launch_decode_sk(p, elem_type(pool->dtype), D, cus, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -304,6 +305,112 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            hipStream_t stream) {
   return decode_call(pool, q, q_dtype, num_tables, rows_per_table, num_q_heads, block_table, table_stride, kv_lens,
                      max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 0, stream);
+}
+
+size_t pkv_attn_decode_shared_prefix_workspace_bytes(int32_t groups, int32_t samples, int32_t q_len,
+                                                     int32_t num_q_heads, int32_t head_dim, int32_t max_prefix_len) {
+  if (groups < 0 || samples < 1 || q_len < 1 || num_q_heads < 1 || head_dim < 1 || max_prefix_len < 0) return 0;
+  const int64_t states = plan_decode(max_prefix_len).splits + 1;
+  const int64_t rows = (int64_t)groups * samples * q_len;
+  return (size_t)(states * rows * num_q_heads * (int64_t)(head_dim + 1) * (int64_t)sizeof(float));
+}
+
+pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t groups,
+                                         int32_t samples, int32_t q_len, int32_t num_q_heads,
+                                         const int32_t* prefix_table, int32_t prefix_stride,
+                                         const int32_t* prefix_lens, int32_t max_prefix_len,
+                                         const int32_t* tail_table, int32_t tail_stride, const int32_t* tail_lens,
+                                         int32_t max_tail_len, float sm_scale, void* out, pkv_dtype out_dtype,
+                                         float* out_lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
+  if (groups < 0 || samples < 1 || q_len < 1 || num_q_heads < 1 || prefix_stride < 1 || tail_stride < 1 ||
+      max_prefix_len < 0 || max_tail_len < 0 || !(sm_scale > 0.f) || sm_scale > 3.0e38f)
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_prefix_len > (int64_t)prefix_stride * pool->page_size ||
+      (int64_t)max_tail_len > (int64_t)tail_stride * pool->page_size)
+    return PKV_ERR_SHAPE;
+  if ((int64_t)groups * samples * q_len > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (groups == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!q || !prefix_table || !prefix_lens || !tail_table || !tail_lens || !out || !workspace) return PKV_ERR_NULL;
+  const int D = pool->head_dim;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype != PKV_BF16 || pool->dtype == PKV_F32 || out_dtype == PKV_FP8_E4M3FN) return PKV_ERR_UNSUPPORTED;
+  const int es = elem_bytes(pool->dtype);
+  if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * es) % 16 != 0 || !aligned(q, 16) ||
+      !aligned(out, 16) || !aligned(workspace, 16))
+    return PKV_ERR_ALIGN;
+  const size_t need = pkv_attn_decode_shared_prefix_workspace_bytes(groups, samples, q_len, num_q_heads, D,
+                                                                    max_prefix_len);
+  if (workspace_bytes < need) return PKV_ERR_SHAPE;
+
+  const SplitPlan plan = plan_decode(max_prefix_len);
+  const int64_t rows = (int64_t)groups * samples * q_len;
+  const int64_t plane = rows * num_q_heads;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = ws_o + (int64_t)(plan.splits + 1) * plane * D;
+
+  DecodeParams pre;
+  pre.k_pool = pool->k;
+  pre.v_pool = pool->v;
+  pre.k_scale = pool->k_scale;
+  pre.v_scale = pool->v_scale;
+  pre.q = q;
+  pre.table = prefix_table;
+  pre.kv_lens = prefix_lens;
+  pre.out = nullptr;
+  pre.out_lse = nullptr;
+  pre.ws_o = ws_o;
+  pre.ws_lse = ws_lse;
+  pre.ws_cum = nullptr;
+  pre.page_stride = pool->page_stride;
+  pre.page_shift = log2i(pool->page_size);
+  pre.num_kv_heads = pool->num_kv_heads;
+  pre.num_tables = groups;
+  pre.rows_per_table = samples * q_len;
+  pre.num_q_heads = num_q_heads;
+  pre.group = num_q_heads / pool->num_kv_heads;
+  pre.table_stride = prefix_stride;
+  pre.splits = plan.splits;
+  pre.tiles_per_split = plan.tiles_per_split;
+  pre.out_bf16 = 0;
+  pre.n_workers = 0;
+  pre.row_groups = 0;
+  pre.causal = 0;
+  pre.write_state = 1;
+  pre.scale_log2 = sm_scale * 1.4426950408889634f;
+
+  DecodeParams tail = pre;
+  tail.table = tail_table;
+  tail.kv_lens = tail_lens;
+  tail.ws_o = ws_o + (int64_t)plan.splits * plane * D;
+  tail.ws_lse = ws_lse + (int64_t)plan.splits * plane;
+  tail.num_tables = groups * samples;
+  tail.rows_per_table = q_len;
+  tail.table_stride = tail_stride;
+  tail.splits = 1;
+  tail.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(max_tail_len, 32));
+  tail.causal = 1;
+
+  if (launch_shared_prefix(pre, tail, elem_type(pool->dtype), D, stream) != hipSuccess) return PKV_ERR_HIP;
+  MergeParams m;
+  m.o_parts = ws_o;
+  m.lse_parts = ws_lse;
+  m.out = out;
+  m.out_lse = out_lse;
+  m.kv_lens = nullptr;
+  m.rows = rows;
+  m.num_states = plan.splits + 1;
+  m.num_q_heads = num_q_heads;
+  m.head_dim = D;
+  m.rows_per_table = 1;
+  m.keys_per_state = 1;
+  m.out_bf16 = out_dtype == PKV_BF16;
+  return launch_merge(m, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,

@@ -68,6 +68,7 @@ struct DecodeParams {
   int32_t n_workers;          // stream-K workers (set by the launcher)
   int32_t row_groups;         // stream-K: row groups per (table row, kv head)
   int32_t causal;             // rows of a table row are a step's tokens: row i sees len - (n - 1 - i) keys
+  int32_t write_state;        // always leave the normalised state of split s in ws_o / ws_lse (empty too)
   float scale_log2;           // sm_scale * log2(e)
 };
 
@@ -169,6 +170,10 @@ hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, 
 int sk_waves_per_worker(int rows_per_unit);
 hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType q, ElemType kv, int head_dim, hipStream_t stream);
+// n-sample step: one launch of every (prefix split, kv head, group, row group)
+// and (tail, kv head, row group) workgroup, each leaving its state.
+hipError_t launch_shared_prefix(const DecodeParams& pre, const DecodeParams& tail, ElemType kv, int head_dim,
+                                hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);

@@ -689,3 +689,29 @@ def test_decode_step_of_one_token_is_plain_decode():
     a = orc.attn_decode_step(kpool, vpool, q, tables, lens, 0.2, kv_dtype="f32")
     b = orc.attn_decode(kpool, vpool, q, tables, lens, 0.2, kv_dtype="f32")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_shared_prefix_step_equals_step_over_joined_tables():
+    """Prefix keys then tail keys: with whole-page prefixes, a step over the
+    concatenated table row (prefix pages, then tail pages) gives the same
+    attention, token by token (the mathematics of the prefix / tail split)."""
+    rng = np.random.default_rng(33)
+    ps, hkv, hq, d, n, samples = 8, 2, 4, 16, 3, 2
+    kpool = rng.standard_normal((30, ps, hkv, d)).astype(np.float32)
+    vpool = rng.standard_normal((30, ps, hkv, d)).astype(np.float32)
+    prefix_tables = np.array([[3, 9, 14], [20, 1, 7]], dtype=np.int32)
+    prefix_lens = np.array([24, 8], dtype=np.int32)              # whole pages
+    tail_tables = np.array([[0, 2], [4, 5], [6, 8], [10, 11]], dtype=np.int32)
+    tail_lens = np.array([9, 3, 16, 4], dtype=np.int32)           # every tail holds the step's n tokens
+    q = rng.standard_normal((4, n, hq, d)).astype(np.float32)
+    out, lse = orc.attn_decode_shared_prefix(kpool, vpool, q, samples, prefix_tables, prefix_lens, tail_tables,
+                                             tail_lens, 0.25, kv_dtype="f32")
+    full = np.zeros((4, 5), dtype=np.int32)
+    for r in range(4):
+        pp = prefix_tables[r // samples][:prefix_lens[r // samples] // ps]
+        row = np.concatenate([pp, tail_tables[r]])
+        full[r, :len(row)] = row
+    ref, ref_lse = orc.attn_decode_step(kpool, vpool, q, full, prefix_lens[np.arange(4) // samples] + tail_lens,
+                                        0.25, kv_dtype="f32")
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)

@@ -463,3 +463,63 @@ def block_causal_prefill(seed=3, causal_block_size=1560):
     history and its whole block; the last page is 24/32 full; 512-page pool."""
     return make_prefill_case("bf16_block_causal_prefill", seed, 1000 + seed, 1, 1568, [1560], [1024 + 4096],
                              24, 24, 128, 32, causal_block_size, num_pool_pages=512)
+
+
+@dataclass
+class SharedStepCase:
+    name: str
+    pool: Pool
+    q: np.ndarray                # [groups * samples, q_len, Hq, D] bf16 bits
+    samples: int
+    num_q_heads: int
+    sm_scale: float
+    prefix_tables: np.ndarray    # [groups, width] int32
+    prefix_lens: np.ndarray      # [groups] int32
+    tail_tables: np.ndarray      # [groups * samples, width] int32
+    tail_lens: np.ndarray        # [groups * samples] int32
+    new_k: Optional[np.ndarray]  # the step's tokens, scattered before attention (bf16 pools)
+    new_v: Optional[np.ndarray]
+    slots: Optional[np.ndarray]
+
+    @property
+    def q_len(self):
+        return self.q.shape[1]
+
+
+def make_shared_step_case(name, seed, perm_seed, groups, samples, q_len, prefix_lens, tail_lens, num_q_heads,
+                          num_kv_heads, head_dim, page_size, kv_dtype="bf16", extra_cols=1):
+    """n-sample decode step over a permuted pool: group g's shared prefix of
+    ``prefix_lens[g]`` keys and each sample's private tail of ``tail_lens[r]``
+    keys sit on pages of their own (the tails on fresh pages); the step's
+    ``q_len`` tokens are the tail's last keys.  bf16 pools: those tokens are
+    poison until scattered from ``new_k`` / ``new_v`` at ``slots``; fp8 pools:
+    every key is resident.  Dead rows, unowned pages and table padding are
+    poison."""
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int32)
+    tail_lens = np.asarray(tail_lens, dtype=np.int32)
+    n_rows = groups * samples
+    p_pages = [math.ceil(int(x) / page_size) for x in prefix_lens]
+    t_pages = [math.ceil(int(x) / page_size) for x in tail_lens]
+    num_pool_pages = sum(p_pages) + sum(t_pages) + 3
+    page_lists, poison_page, _ = _assign_pages(perm_seed, num_pool_pages, p_pages + t_pages)
+    prefix_tables = _table(page_lists[:groups], max(p_pages + [1]) + extra_cols, poison_page)
+    tail_tables = _table(page_lists[groups:], max(t_pages + [1]) + extra_cols, poison_page)
+    owned = np.concatenate([pl for pl in page_lists if len(pl)])
+    valid = []
+    for L, pages in zip(list(prefix_lens) + list(tail_lens), page_lists):
+        valid += [min(page_size, int(L) - j * page_size) for j in range(len(pages))]
+    pool = _fill_pool(seed, num_pool_pages, page_size, num_kv_heads, head_dim, kv_dtype, owned, valid)
+    new_k = new_v = slots = None
+    if kv_dtype != "fp8":
+        slot_list = [_slot(tail_tables[r], p, page_size)
+                     for r in range(n_rows) for p in range(max(0, int(tail_lens[r]) - q_len), int(tail_lens[r]))]
+        slots = np.asarray(slot_list, dtype=np.int64)
+        flat_k = pool.k.reshape(-1, num_kv_heads, head_dim)
+        flat_v = pool.v.reshape(-1, num_kv_heads, head_dim)
+        new_k, new_v = flat_k[slots].copy(), flat_v[slots].copy()
+        flat_k[slots] = POISON[kv_dtype]
+        flat_v[slots] = POISON[kv_dtype]
+    qf = np.random.Generator(np.random.PCG64(seed + 7)).standard_normal(
+        (n_rows, q_len, num_q_heads, head_dim), dtype=np.float32)
+    return SharedStepCase(name, pool, to_storage(qf, "bf16"), samples, num_q_heads, 1.0 / math.sqrt(head_dim),
+                          prefix_tables, prefix_lens, tail_tables, tail_lens, new_k, new_v, slots)

@@ -393,6 +393,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         acc = f32x16{};
 #pragma unroll
         for (int s2 = 0; s2 < KSTEPS; ++s2) acc = mfma32x32x16_bf16(a[s2], q[s2], acc);
+        // Keep 4 K operand reads in flight ahead of the MFMA chain.  Left to
+        // itself the scheduler (at the register limit) issues each read right
+        // before its MFMA and waits for it.  (The fp8 kernel, with its
+        // widening pass, has no registers to spare for it.)
+        if constexpr (!kFp8) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // 4 LDS reads
+#pragma unroll
+          for (int i = 0; i < KSTEPS - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);   // the last 4 MFMAs
+        }
       };
       // O^T += V^T P^T over this wave's key half of V tile t; pk[mu] is the bf16
       // P of keys 32 kh + 16 mu + 8 (j / 4) + 4 hf + (j % 4), j = 0..7.  Lane

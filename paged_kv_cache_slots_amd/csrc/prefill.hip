@@ -327,6 +327,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         __syncthreads();
       };
       cache_pages(page_base);
+      // Page ids of this wave's DMA rows for tiles tw0 .. tw0 + 63, one per
+      // lane (read back with readlane: no LDS round trip per DMA).  Reloaded
+      // when the DMA lookahead passes the window or the page cache moves;
+      // entries past the cached pages are never used before a reload.
+      int tw0 = t0, win = 0;
+      auto load_window = [&](int tb) {
+        const int key = min((tb + lane) * kKT + 8 * wave, x.kmax - 1);
+        win = pages[min((key >> shift) - page_base, kTableCache - 1)];
+        tw0 = tb;
+      };
+      load_window(t0);
 
       // LDS-DMA of tile t of K or V into its stage: this wave writes rows
       // 8 wave .. 8 wave + 7 (one page: page_size >= 16).  Keys past the unit's
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const bool live = t < t1;
         const int kmax1 = x.kmax - 1;
         int pg = 0;
-        if (live) pg = __builtin_amdgcn_readfirstlane(pages[(min(t * kKT + 8 * wave, kmax1) >> shift) - page_base]);
+        if (live) pg = __builtin_amdgcn_readlane(win, t - tw0);
         const uint8_t* base = pool_b + (int64_t)pg * page_stride_b + head_off_b;
 #pragma unroll
         for (int j = 0; j < S::IPW; ++j) {
@@ -490,8 +501,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         }
         if (need_refresh) {
           const int last_t = t + 3 < t1 ? t + 3 : t1 - 1;
-          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) cache_pages((t * kKT) >> shift);
+          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) {
+            cache_pages((t * kKT) >> shift);
+            load_window(t);
+          }
         }
+        if (t + 3 >= tw0 + 64) load_window(t);
         // refill: K(t+3) into K(t)'s stage, V(t+1) into V(t-2)'s stage
         dma_tile(kpool_b, kstage(t + 3), t + 3, true);
         dma_tile(vpool_b, vstage(t + 1), t + 1, false);

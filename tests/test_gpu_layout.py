@@ -142,13 +142,14 @@ class Rollout:
         pkv.pkv_causal_layout(self.lay, self.table, self.priv, self.committed, self.evicted)
         pkv.pkv_copy_slots(self.pool, self.lay.commit_src, self.lay.commit_dst)
 
-    def forward(self, k_new, v_new, q):
+    def forward(self, k_new, v_new, q, out=None):
         """k_new / v_new [T, Hkv, D] and q [T, Hq, D] bf16 on the device."""
         lay = self.lay
         pkv.pkv_scatter_slots(self.pool, k_new, v_new, lay.stage_slots, slots2=lay.stage_slots2)
         pkv.pkv_copy_slots(self.pool, lay.current_src, lay.current_dst)
         nb, cbs = len(self.sizes), self.sizes[0]
-        out = torch.empty((nb, cbs, self.hq, self.d), dtype=torch.float32, device=DEV)
+        if out is None:
+            out = torch.empty((nb, cbs, self.hq, self.d), dtype=torch.float32, device=DEV)
         max_keys = self.pin + self.window + cbs
         pkv.pkv_attn_prefill_block_causal(self.pool, q.view(nb, cbs, self.hq, self.d), lay.block_tables,
                                           lay.n_ctx, lay.seq_len, 0, max_keys, 1.0 / math.sqrt(self.d), out)
@@ -237,3 +238,53 @@ def test_exact_window_zero_query_one_hot_values_show_the_visible_keys():
                     assert seen == set(vis), f"committed {c} block {b}: {sorted(seen ^ set(vis))}"
                     np.testing.assert_allclose(got[b, i, h], want, rtol=1e-2, atol=1e-6)
         ro.commit(cbs)
+
+
+def test_exact_window_forward_graph_replays_across_commits():
+    """The forward (scatter, current copies, per-block prefill) reads only
+    device tensors that each commit rewrites in place, so one captured graph
+    serves every commit: capture once, then per commit run the commit eagerly,
+    refill the static inputs, replay and compare with float64 attention."""
+    ps, pin, window, cbs, nb, hq, hkv, d = 32, 40, 100, 24, 3, 4, 2, 128
+    sizes, total = [cbs] * nb, cbs * nb
+    rng = np.random.default_rng(77)
+    n_keys = 6 * total
+    keys = to_storage(rng.standard_normal((n_keys, hkv, d)).astype(np.float32), "bf16")
+    vals = to_storage(rng.standard_normal((n_keys, hkv, d)).astype(np.float32), "bf16")
+    qs = to_storage(rng.standard_normal((6, total, hq, d)).astype(np.float32), "bf16")
+    ro = Rollout(21, ps, pin, window, sizes, hq, hkv, d)
+    ro.commit_layout()
+    kbuf = torch.empty((total, hkv, d), dtype=torch.bfloat16, device=DEV)
+    vbuf, qbuf = torch.empty_like(kbuf), torch.empty((total, hq, d), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((nb, cbs, hq, d), dtype=torch.float32, device=DEV)
+
+    def fill(step):
+        c = ro.committed
+        kbuf.copy_(to_dev(keys[c:c + total]))
+        vbuf.copy_(to_dev(vals[c:c + total]))
+        qbuf.copy_(to_dev(qs[step]))
+        torch.cuda.synchronize()
+
+    def check(step, what):
+        c = ro.committed
+        ref = _dense_reference(as_f64(keys), as_f64(vals), as_f64(qs[step]), c, sizes, pin, window, hq, hkv)
+        assert_close(from_dev(out), ref, "bf16", f"{what} step {step} (committed {c})")
+
+    note("exact window graph: eager forward, then capture")
+    fill(0)
+    ro.forward(kbuf, vbuf, qbuf, out=out)
+    torch.cuda.synchronize()
+    check(0, "eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ro.forward(kbuf, vbuf, qbuf, out=out)
+    torch.cuda.synchronize()
+    for step in range(1, 6):
+        ro.commit(total)                      # eager: rotate, lay out, fill private pages
+        fill(step)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        note(f"exact window graph replay step {step} committed={ro.committed} evicted={ro.evicted}")
+        graph.replay()
+        torch.cuda.synchronize()
+        check(step, "replay")

@@ -5,16 +5,21 @@
  * Sources (page titles and sections):
  *   [P1] "Paged causal K/V cache and cached attention for VisualGen":
  *        Description / Cache, Description / Attention, Per-File QA
- *        Perspective, and the review thread on staged-token slot ids.
+ *        Perspective, and the review threads on staged-token slot ids, on
+ *        power-of-two pages and on the private-page regions
+ *        (committed_private / current_private).
  *   [P5] "Support shared-prefix attention for n-sample requests in FMHA":
- *        commit messages on the FA4 prefix and tail passes, small-batch
+ *        commit messages on the n-sample path with CUDA graphs (up to 16
+ *        query tokens per row), the FA4 prefix and tail passes, small-batch
  *        splits, MIN_SPLIT_TOKENS and the grouping check.
  *
  * Conventions shared by every call
  * --------------------------------
- * - All pointers except `pool` and the `pkv_pool` struct itself are DEVICE
- *   pointers.  The caller owns every buffer; the library allocates no device
- *   memory and keeps no state between calls.
+ * - All pointers are DEVICE pointers except `pool` (and the `pkv_pool`
+ *   struct itself) and those a declaration marks HOST (block sizes and
+ *   sizing results of the exact-window layout).  The caller owns every
+ *   buffer; the library allocates no device memory and keeps no state
+ *   between calls beyond a per-device cache of the compute-unit count.
  * - Every call is asynchronous on `stream` and never synchronises with the
  *   host, so a captured HIP graph replays it after the caller edits the
  *   device-side lengths, tables or slots in place ([P1] Description / Cache,
@@ -395,7 +400,8 @@ typedef struct {
 #define PKV_MAX_CAUSAL_BLOCKS 64
 
 /*
- * pkv_causal_layout_bounds -- sizes an exact-window geometry needs (host only).
+ * pkv_causal_layout_bounds -- sizes an exact-window geometry needs (host only:
+ * block_sizes is a HOST int32 [num_blocks] array, bounds a HOST struct).
  *   rolling_pages = ceil((window + page_size - 1 + sum(block_sizes)) / page_size)
  *   private_pages = ceil((3 (page_size - 1) + max(block_sizes)) / page_size)
  *   table_width   = pin / page_size + window / page_size + private_pages

@@ -657,19 +657,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   }
 }
 
-// Merge of the split leftover units: workgroup (xcd, k) of a grid of
-// 8 x kMaxTailUnits combines the pieces of leftover unit k of XCD xcd with
-// the log-sum-exp merge, in key order.  The piece of chunk w sits in slot 2 w'
-// of the main kernel's workgroup w' = xcd + 8 w, or in slot 2 w' + 1 when it
-// is not the first segment of that chunk.  Thread (g, rb, lane) owns values
-// 16 g .. 16 g + 15 of the slot rows of row block rb and lane, so each load
-// instruction reads 256 contiguous bytes; piece loads go out 4 at a time.
+// Merge of the split leftover units: workgroup (rb, k, xcd) of a grid of
+// 4 x kMaxTailUnits x 8 combines, for row block rb, the pieces of leftover
+// unit k of XCD xcd with the log-sum-exp merge, in key order.  The piece of
+// chunk w sits in slot 2 w' of the main kernel's workgroup w' = xcd + 8 w, or
+// in slot 2 w' + 1 when it is not the first segment of that chunk.  Thread
+// (g, lane) owns values 16 g .. 16 g + 15 of the slot rows of row block rb
+// and lane, so each load instruction reads 256 contiguous bytes; piece loads
+// go out 4 at a time.  (One workgroup per row block rather than per unit:
+// the merge is bound by load latency, so it wants many small workgroups.)
 template <int D>
-__global__ __launch_bounds__(256 * (D / 32)) void prefill_merge_kernel(PrefillParams p, int main_grid) {
+__global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillParams p, int main_grid) {
   constexpr int PB = 4;   // pieces per batch of loads
   __shared__ int32_t tcum[kMaxTailUnits + 1];
   const int xcd = blockIdx.x & 7;
-  const int k = blockIdx.x >> 3;
+  const int k = (blockIdx.x >> 3) % kMaxTailUnits;
+  const int rb = (blockIdx.x >> 3) / kMaxTailUnits;
   const int Gx = main_grid >> 3;
   const XcdPlan plan = xcd_plan(p, xcd, Gx);
   if (!plan.sk || k >= plan.nt) return;
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(256 * (D / 32)) void prefill_merge_kernel(PrefillPa
   const int64_t w0 = F / C, w1 = (F + ut - 1) / C;
   if (w0 == w1) return;   // one chunk held the whole unit: stored by the main kernel
 
-  const int lane = threadIdx.x & 63, rb = (threadIdx.x >> 6) & 3, g = threadIdx.x >> 8;
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const float* base = p.ws_o + (rb * 65) * 64 + lane;
   auto slot = [&](int64_t w) {
     return base + (2 * (xcd + 8 * w) + ((w == w0 && F != w0 * C) ? 1 : 0)) * (int64_t)kSlotFloats;
@@ -770,9 +773,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
   }
   if (!any) return e;
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3(8 * kMaxTailUnits), dim3(1024), 0, stream, p, g);
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3(4 * 8 * kMaxTailUnits), dim3(256), 0, stream, p, g);
   else
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3(8 * kMaxTailUnits), dim3(512), 0, stream, p, g);
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3(4 * 8 * kMaxTailUnits), dim3(128), 0, stream, p, g);
   return hipGetLastError();
 }
 

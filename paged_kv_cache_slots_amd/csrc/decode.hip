@@ -672,34 +672,36 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_pe
       const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
       return slot * rows_w + row_in;
     };
-    float m = kNegInf;
+    // one pass (LSE and outputs of PB pieces loaded together); the running
+    // sums are rescaled when the running max grows
+    float m = kNegInf, wsum = 0.f;
     for (int64_t w = w0; w <= w1; w += PB) {
       float l[PB];
+      f32x4 v[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) l[j] = w + j <= w1 ? p.ws_lse[slot_row(w + j)] : kNegInf;
+      for (int j = 0; j < PB; ++j) {
+        const bool ok = w + j <= w1;
+        const int64_t sr = slot_row(ok ? w + j : w1);
+        l[j] = ok ? p.ws_lse[sr] : kNegInf;
+        v[j] = *reinterpret_cast<const f32x4*>(p.ws_o + sr * D + 4 * ch);
+      }
+      float mb = m;
 #pragma unroll
-      for (int j = 0; j < PB; ++j) m = fmaxf(m, l[j]);
+      for (int j = 0; j < PB; ++j) mb = fmaxf(mb, l[j]);
+      if (mb == kNegInf) continue;
+      const float sc = m == kNegInf ? 0.f : fast_exp2((m - mb) * kLog2e);
+      acc *= sc;
+      wsum *= sc;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        // every piece holds keys, so its state is finite; padding entries weigh 0
+        const float f = l[j] == kNegInf ? 0.f : fast_exp2((l[j] - mb) * kLog2e);
+        acc += f * v[j];
+        wsum += f;
+      }
+      m = mb;
     }
     if (m != kNegInf) {
-      float wsum = 0.f;
-      for (int64_t w = w0; w <= w1; w += PB) {
-        float l[PB];
-        f32x4 v[PB];
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-          const bool ok = w + j <= w1;
-          const int64_t sr = slot_row(ok ? w + j : w1);
-          l[j] = ok ? p.ws_lse[sr] : kNegInf;
-          v[j] = *reinterpret_cast<const f32x4*>(p.ws_o + sr * D + 4 * ch);
-        }
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-          // every piece holds keys, so its state is finite; padding entries weigh 0
-          const float f = l[j] == kNegInf ? 0.f : fast_exp2((l[j] - m) * kLog2e);
-          acc += f * v[j];
-          wsum += f;
-        }
-      }
       acc *= 1.0f / wsum;
       lse_out = m + fast_log2(wsum) * kLn2;
     }

@@ -688,38 +688,41 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillPar
   auto slot = [&](int64_t w) {
     return base + (2 * (xcd + 8 * w) + ((w == w0 && F != w0 * C) ? 1 : 0)) * (int64_t)kSlotFloats;
   };
-  float m_all = kNegInf;
-  for (int64_t w = w0; w <= w1; w += PB) {
-    float l[PB];
-#pragma unroll
-    for (int j = 0; j < PB; ++j) l[j] = w + j <= w1 ? slot(w + j)[64 * 64] : kNegInf;
-#pragma unroll
-    for (int j = 0; j < PB; ++j) m_all = fmaxf(m_all, l[j]);
-  }
+  // one pass (LSE and values of PB pieces loaded together); the running sums
+  // are rescaled when the running max grows
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (m_all != kNegInf) {
-    for (int64_t w = w0; w <= w1; w += PB) {
-      float f[PB], v[PB][16];
+  float m_all = kNegInf, wsum = 0.f;
+  for (int64_t w = w0; w <= w1; w += PB) {
+    float f[PB], v[PB][16];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const bool ok = w + j <= w1;
-        const float* pw = slot(ok ? w + j : w1);
-        f[j] = ok ? pw[64 * 64] : kNegInf;
+    for (int j = 0; j < PB; ++j) {
+      const bool ok = w + j <= w1;
+      const float* pw = slot(ok ? w + j : w1);
+      f[j] = ok ? pw[64 * 64] : kNegInf;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[j][i] = pw[(16 * g + i) * 64];
-      }
-#pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        // a piece with lse -inf has no keys (its values are zero): weight 0
-        const float e = f[j] == kNegInf ? 0.f : fast_exp2((f[j] - m_all) * kLog2e);
-        wsum += e;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += e * v[j][i];
-      }
+      for (int i = 0; i < 16; ++i) v[j][i] = pw[(16 * g + i) * 64];
     }
+    float mb = m_all;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) mb = fmaxf(mb, f[j]);
+    if (mb == kNegInf) continue;
+    const float sc = m_all == kNegInf ? 0.f : fast_exp2((m_all - mb) * kLog2e);
+    wsum *= sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] *= sc;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      // a piece with lse -inf has no keys (its values are zero): weight 0
+      const float e = f[j] == kNegInf ? 0.f : fast_exp2((f[j] - mb) * kLog2e);
+      wsum += e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += e * v[j][i];
+    }
+    m_all = mb;
+  }
+  if (m_all != kNegInf) {
     const float inv = 1.0f / wsum;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] *= inv;

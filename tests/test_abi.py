@@ -198,3 +198,50 @@ def _layout_call(**kw):
 ])
 def test_causal_layout_argument_checks(kw, expect):
     assert _layout_call(**kw) == expect
+
+
+def test_decode_step_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+
+    def call(pool, **kw):
+        a = dict(q=A, qd=pkv.PKV_BF16, T=4, n=9, hq=32, table=A, ts=128, lens=A, maxlen=4096, scale=0.1, out=A,
+                 od=pkv.PKV_BF16)
+        a.update(kw)
+        return lib.pkv_attn_decode_step(ctypes.byref(pool), a["q"], a["qd"], a["T"], a["n"], a["hq"], a["table"],
+                                        a["ts"], a["lens"], a["maxlen"], a["scale"], a["out"], a["od"], None, None, 0,
+                                        None)
+    assert call(p, lens=None) == 1
+    assert call(p, n=0) == 2
+    assert call(p, hq=12) == 2
+    assert call(p, maxlen=128 * 32 + 1) == 2
+    assert call(p, scale=0.0) == 2
+    assert call(p, qd=pkv.PKV_FP8_E4M3FN) == 4
+    assert call(_pool(page_size=8, page_stride=8 * 8 * 128), maxlen=512) == 4
+    assert call(p, T=0) == 0
+
+
+def test_decode_shared_prefix_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+
+    def call(pool, **kw):
+        a = dict(q=A, qd=pkv.PKV_BF16, G=8, S=16, n=1, hq=32, pt=A, ps=64, pl=A, mp=2048, tt=A, ts=16, tl=A, mt=512,
+                 scale=0.1, out=A, od=pkv.PKV_BF16, ws=A, wsb=1 << 30)
+        a.update(kw)
+        return lib.pkv_attn_decode_shared_prefix(
+            ctypes.byref(pool), a["q"], a["qd"], a["G"], a["S"], a["n"], a["hq"], a["pt"], a["ps"], a["pl"], a["mp"],
+            a["tt"], a["ts"], a["tl"], a["mt"], a["scale"], a["out"], a["od"], None, a["ws"], a["wsb"], None)
+    assert call(p, ws=None) == 1
+    assert call(p, tl=None) == 1
+    assert call(p, S=0) == 2
+    assert call(p, n=0) == 2
+    assert call(p, mp=64 * 32 + 1) == 2
+    assert call(p, mt=16 * 32 + 1) == 2
+    need = pkv.pkv_attn_decode_shared_prefix_workspace_bytes(8, 16, 1, 32, 128, 2048)
+    assert need == 5 * 128 * 32 * 129 * 4
+    assert call(p, wsb=need - 1) == 2
+    assert call(p, qd=pkv.PKV_F32) == 4
+    assert call(_pool(dtype=pkv.PKV_F32, page_stride=32 * 8 * 128)) == 4
+    assert call(p, ws=A + 8) == 6
+    assert call(p, G=0) == 0

@@ -460,6 +460,27 @@ pkv_status pkv_causal_layout(const int32_t* table, int32_t table_len, const int3
                              int64_t* stage_slots, int64_t* stage_slots2, int64_t* commit_src, int64_t* commit_dst,
                              int64_t* current_src, int64_t* current_dst, int32_t list_stride, hipStream_t stream);
 
+/*
+ * Device-side content checks (debugging aid).
+ * [P1] Per-File QA Perspective (the scatter does not range-check device slot
+ * ids; device slot bounds stay the caller's responsibility).  The attention
+ * and copy calls trust their device inputs; these calls count the entries
+ * that break that contract, reading only ids and lengths, never the pool.
+ * One workgroup walks the input: meant for debugging, not for every step.
+ *
+ * pkv_check_slots: *bad (device int32) = number of slots[i] >= num_pages *
+ *   page_size (negative entries are sentinels, valid).  n == 0 writes 0.
+ * pkv_check_tables: *bad (device int32) = number of rows t whose kv_lens[t]
+ *   is negative or above table_stride * page_size, or whose first
+ *   ceil(kv_lens[t] / page_size) page ids are not all in [0, num_pages).
+ * Both overwrite *bad (no zeroing needed) and run asynchronously on stream.
+ * Errors: bad pool -> as pkv_scatter_slots; NULL -> PKV_ERR_NULL; negative
+ * sizes -> PKV_ERR_SHAPE.
+ */
+pkv_status pkv_check_slots(const pkv_pool* pool, const int64_t* slots, int64_t n, int32_t* bad, hipStream_t stream);
+pkv_status pkv_check_tables(const pkv_pool* pool, const int32_t* block_table, int32_t table_stride,
+                            const int32_t* kv_lens, int32_t num_tables, int32_t* bad, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_attn_decode", "pkv_attn_prefill_workspace_bytes", "pkv_attn_prefill_block_causal",
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
-            "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix"]
+            "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
+            "pkv_check_tables"]
 
 
 class PkvError(RuntimeError):
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_attn_decode_shared_prefix_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_decode_shared_prefix": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, I32, P, I32, P, I32, P,
                                                          I32, P, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
+        "pkv_check_slots": (ctypes.c_int, [PP, P, I64, P, P]),
+        "pkv_check_tables": (ctypes.c_int, [PP, P, I32, P, I32, P, P]),
         "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
                                                          P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
@@ -352,3 +355,26 @@ def pkv_causal_layout(layout: CausalLayout, table: torch.Tensor, private_pages: 
         L.block_tables.shape[1], L.n_ctx.data_ptr(), L.seq_len.data_ptr(), L.stage_slots.data_ptr(),
         L.stage_slots2.data_ptr(), L.commit_src.data_ptr(), L.commit_dst.data_ptr(), L.current_src.data_ptr(),
         L.current_dst.data_ptr(), L.bounds["list_stride"], _stream(stream)))
+
+
+def pkv_check_slots(pool: Pool, slots: torch.Tensor, stream=None) -> torch.Tensor:
+    """Device int32 tensor [1]: how many int64 ``slots`` point past the pool
+    (negative sentinels are valid).  Asynchronous; read it after a sync."""
+    bad = torch.empty(1, dtype=torch.int32, device=slots.device)
+    ps = pool.struct()
+    _check("pkv_check_slots", load_library().pkv_check_slots(ctypes.byref(ps), slots.data_ptr(), slots.numel(),
+                                                             bad.data_ptr(), _stream(stream)))
+    return bad
+
+
+def pkv_check_tables(pool: Pool, block_table: torch.Tensor, kv_lens: torch.Tensor, stream=None) -> torch.Tensor:
+    """Device int32 tensor [1]: how many table rows have a length or a used
+    page id that would read outside the pool."""
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [rows, width] with contiguous rows")
+    bad = torch.empty(1, dtype=torch.int32, device=block_table.device)
+    ps = pool.struct()
+    _check("pkv_check_tables", load_library().pkv_check_tables(
+        ctypes.byref(ps), block_table.data_ptr(), block_table.stride(0), kv_lens.data_ptr(), block_table.shape[0],
+        bad.data_ptr(), _stream(stream)))
+    return bad

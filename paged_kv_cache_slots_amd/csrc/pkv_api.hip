@@ -637,4 +637,26 @@ pkv_status pkv_causal_layout(const int32_t* table, int32_t table_len, const int3
   return launch_causal_layout(p, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+pkv_status pkv_check_slots(const pkv_pool* pool, const int64_t* slots, int64_t n, int32_t* bad, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (n < 0) return PKV_ERR_SHAPE;
+  if (!bad || (n > 0 && !slots)) return PKV_ERR_NULL;
+  const int64_t capacity = pool->num_pages * (int64_t)pool->page_size;
+  return launch_check_slots(slots, n, capacity, bad, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_check_tables(const pkv_pool* pool, const int32_t* block_table, int32_t table_stride,
+                            const int32_t* kv_lens, int32_t num_tables, int32_t* bad, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_tables < 0 || table_stride < 1) return PKV_ERR_SHAPE;
+  if (!bad || (num_tables > 0 && (!block_table || !kv_lens))) return PKV_ERR_NULL;
+  return launch_check_tables(block_table, table_stride, kv_lens, num_tables, log2i(pool->page_size),
+                             pool->num_pages, bad, stream) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 }  // extern "C"

@@ -179,6 +179,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_coun
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);
 hipError_t launch_copy_slots(const CopySlotsParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_causal_layout(const LayoutParams& p, hipStream_t stream);
+hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t capacity, int32_t* bad, hipStream_t stream);
+hipError_t launch_check_tables(const int32_t* table, int32_t stride, const int32_t* lens, int32_t rows,
+                               int32_t page_shift, int64_t num_pages, int32_t* bad, hipStream_t stream);
 int64_t prefill_units(int32_t batch, int32_t s_q, int32_t num_q_heads);
 size_t prefill_slot_bytes();
 

@@ -245,3 +245,16 @@ def test_decode_shared_prefix_argument_checks():
     assert call(_pool(dtype=pkv.PKV_F32, page_stride=32 * 8 * 128)) == 4
     assert call(p, ws=A + 8) == 6
     assert call(p, G=0) == 0
+
+
+def test_check_calls_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+    assert lib.pkv_check_slots(ctypes.byref(p), A, 10, None, None) == 1
+    assert lib.pkv_check_slots(ctypes.byref(p), None, 10, A, None) == 1
+    assert lib.pkv_check_slots(ctypes.byref(p), A, -1, A, None) == 2
+    assert lib.pkv_check_tables(ctypes.byref(p), A, 0, A, 4, A, None) == 2
+    assert lib.pkv_check_tables(ctypes.byref(p), A, 8, A, -1, A, None) == 2
+    assert lib.pkv_check_tables(ctypes.byref(p), None, 8, A, 4, A, None) == 1
+    bad = _pool(page_size=48)
+    assert lib.pkv_check_tables(ctypes.byref(bad), A, 8, A, 4, A, None) == 2

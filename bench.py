@@ -484,6 +484,43 @@ def cpu_baseline(case, seconds):
 
 # ----------------------------------------------------------------------------- main
 
+def device_info(torch, pkv):
+    """The GPU as the runtime reports it, and the peaks derived from it beside
+    the published ones: bf16 dense MFMA = CUs x clock x 4096 flop per clock."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    clock_khz = None
+    # the HIP runtime libpkv is linked to (the process's only one), through libpkv's handle
+    get_attr = getattr(pkv.load_library(), "hipDeviceGetAttribute", None)
+    if get_attr is not None:
+        v = ctypes.c_int(0)
+        if get_attr(ctypes.byref(v), 5, 0) == 0:   # hipDeviceAttributeClockRate, kHz
+            clock_khz = v.value
+    cus = int(props.multi_processor_count)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": cus,
+            "max_clock_mhz": None if clock_khz is None else clock_khz / 1000.0,
+            "memory_gib": round(props.total_memory / 2**30, 1),
+            "spec_peaks": {"hbm_gbs": HBM_PEAK_GBS, "bf16_mfma_tflops": BF16_MFMA_PEAK_TFLOPS}}
+    if clock_khz:
+        info["derived_bf16_mfma_tflops"] = round(cus * clock_khz * 1e3 * 4096 / 1e12, 1)
+    return info
+
+
+def copy_ceiling(torch, mib=1024):
+    """Achievable streaming bandwidth: a device copy of MIB MiB (read + write),
+    median of 10; reported against the HBM peak, which stays the roofline."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    med, _, _ = time_events(torch, lambda: dst.copy_(src), 10)
+    gbs = 2 * (mib << 20) / (med * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"what": f"device copy of {mib} MiB (read + write)", "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -531,6 +568,8 @@ def main():
                      "kernel": "pkv_attn_decode call (decode kernel + split merge kernel)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
         "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],
+        "device": device_info(torch, pkv),
+        "copy_ceiling": copy_ceiling(torch),
     }
     workloads = {}
     flush = Flusher(torch)

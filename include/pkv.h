@@ -272,11 +272,13 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
  *                      and merged by a second kernel on the same stream; with
  *                      NULL (or too small / misaligned) they run whole.  Two
  *                      calls in flight at once need two workspaces.
- * Kernel: bf16 MFMA.  K/V bf16 (head_dim 128 or 64, page_size >= 16), or
+ * Kernel: K/V bf16 (head_dim 128 or 64, page_size >= 16) on bf16 MFMA, or
  * fp8 e4m3fn with k_scale / v_scale (head_dim 128, page_size >= 32): the fp8
- * rows are moved to LDS as they are, widened to bf16 exactly in LDS, and the
- * scale of each (page, kv head) is applied in the softmax (K scale on the
- * scores, V scale on the probabilities and back out of their sum).  Scales
+ * rows are moved to LDS as they are; QK^T runs on fp8 MFMA from the raw K
+ * codes, with q held per row as two e4m3 code sets (about 2^-8 relative,
+ * near bf16's own rounding), and PV on bf16 MFMA over V widened exactly in
+ * LDS.  The scale of each (page, kv head) is applied in the softmax (K scale
+ * on the scores, V scale on the probabilities and back out of their sum).  Scales
  * must be >= 0; a scale below 2^-100 acts as 2^-100 (so 0 gives keys of
  * score 0 and values of weight ~0, as code x 0 would, without 0 x inf).
  * Errors: as pkv_attn_decode; fp8 with another head_dim or page_size, or an

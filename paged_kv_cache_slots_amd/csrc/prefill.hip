@@ -35,6 +35,13 @@
 //     The loop is unrolled by two so score and P registers trade roles
 //     instead of being copied; MFMAs are built in their VGPR form so the
 //     scores feed the vector ALUs without accumulator-register moves.
+//   * fp8 e4m3fn pools: the LDS-DMA copies raw codes (half the bytes).  QK^T
+//     runs on 32x32x64 fp8 MFMAs straight from the raw K tile, with Q held
+//     as two e4m3 code sets per row (hi, and 16x the residual through the
+//     MFMA's 2^-4 block scale), so scores carry about 2^-8 relative error;
+//     the page's K scale and Q's row scale multiply the scores.  Each step
+//     widens the next V tile to bf16 in LDS (exactly) for the bf16 PV, whose
+//     P carries the page's V scale in its exponent.
 //   * Loads never branch: keys at or past the unit's last visible key re-read
 //     that key (finite; its score is masked, its P is exactly 0), so dead page
 //     slots and table entries past the last page never reach a product.
@@ -67,8 +74,8 @@ constexpr int kSlotFloats = 4 * 65 * 64;   // partial state: [row block][64 outp
 
 // LDS of one workgroup.  bf16 pools: the LDS-DMA writes the bf16 tiles the
 // MFMAs read, NST stages each of K and V.  fp8 pools: the LDS-DMA writes raw
-// fp8 tiles (NST stages each); each step converts the tiles it needs into one
-// bf16 K tile and one bf16 V tile, which the MFMAs read.
+// fp8 tiles (NST stages each); the fp8 QK^T MFMAs read the raw K tiles, and
+// each step converts the V tile the next PV needs into one bf16 V tile.
 template <int D, bool kFp8>
 struct PSmem {
   static constexpr int ROWB = D * 2;              // bytes of one bf16 key row in LDS (no padding: XOR swizzle)
@@ -77,11 +84,11 @@ struct PSmem {
   static constexpr int CH = DROWB / 16;           // 16-byte chunks per DMA row
   static constexpr int DTB = kKT * DROWB;         // bytes of one DMA tile
   static constexpr int NST = 3;                   // DMA pipeline stages of each of K and V
-  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? 2 * TB : 0);   // K stages, V stages, bf16 K and V
+  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? TB : 0);   // K stages, V stages, bf16 V
   static constexpr int RPI = 1024 / DROWB;        // rows written by one LDS-DMA instruction (64 lanes x 16 B)
   static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
   static_assert(RPI * IPW == 8, "a wave writes 8 rows of each tile");
-  static_assert(!kFp8 || kKT * CH == kThreads, "one 16-byte fp8 chunk of each of K and V per thread");
+  static_assert(!kFp8 || kKT * CH == kThreads, "one 16-byte fp8 chunk of the V tile per thread");
   static constexpr int COMBINE = 4 * 66 * 64 * 4;   // key-half join: [row block][64 + 2 values][lane] floats
   static constexpr int BYTES = STAGES > COMBINE ? STAGES : COMBINE;
 };
@@ -95,8 +102,12 @@ template <int D>
 __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 2 * ((r >> 1) & 1); }
+// Raw fp8 K rows (128 bytes, two to a 256-byte bank line): the 16 rows of a
+// 16-lane operand read land on 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swz_k8(int r) { return (r >> 1) & 7; }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // One LDS-DMA instruction (buffer_load_dwordx4 ... lds): every lane copies 16
 // bytes at byte offset voff of the buffer [base, base + nbytes) to LDS address
@@ -293,14 +304,59 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     const int wrow0 = x.row0 + 32 * rb;
     const int wmin = (wrow0 + 31 < x.seq) ? visible_keys(wrow0, x.n_ctx, x.seq, x.cbs) : 0;
 
-    // Q operand of this row block: row ln, dims 16 s + 8 hf .. +8
+    // Q operand of this row block.  bf16 pools: row ln, dims 16 s + 8 hf .. +8
+    // (bf16 MFMA).  fp8 pools: row ln, dims 64 j + 32 hf .. +32 (fp8 MFMA;
+    // K's operand takes the same dims) as two e4m3 code sets with one scale
+    // per row: with v = q / qsc (the row's largest |q| maps to 448),
+    // hi = e4m3(v) and lo = e4m3(16 (v - hi)), so v = hi + lo / 16 to about
+    // 2^-8 relative, near bf16's own rounding.
     u32x4 q[KSTEPS];
+    i32x8_t q8[2], q8l[2];
+    float qsc = 1.f;
     {
       const bool ok = my_row < x.seq;
       const uint16_t* qp =
           p.q + ((int64_t)x.b * p.s_q + (ok ? my_row : 0)) * p.q_tok_stride + (int64_t)x.h * p.q_head_stride;
+      if constexpr (!kFp8) {
 #pragma unroll
-      for (int s2 = 0; s2 < KSTEPS; ++s2) q[s2] = ok ? ld16(qp + 16 * s2 + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
+        for (int s2 = 0; s2 < KSTEPS; ++s2) q[s2] = ok ? ld16(qp + 16 * s2 + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        u32x4 raw[2][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            raw[j][w] = ok ? ld16(qp + 64 * j + 32 * hf + 8 * w) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[j][w][e] << 16)),
+                                       fabsf(__uint_as_float(raw[j][w][e] & 0xffff0000u))));
+          }
+        {
+          // lanes l and l ^ 32 hold the two halves of one row
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+          amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+        qsc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            // code word k: dims 64 j + 32 hf + 4 k .. + 3, as bytes 0..3
+            const uint32_t w0 = raw[j][k >> 1][2 * (k & 1)], w1 = raw[j][k >> 1][2 * (k & 1) + 1];
+            const float v0 = __uint_as_float(w0 << 16) * inv, v1 = __uint_as_float(w0 & 0xffff0000u) * inv;
+            const float v2 = __uint_as_float(w1 << 16) * inv, v3 = __uint_as_float(w1 & 0xffff0000u) * inv;
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, wd, true);
+            q8[j][k] = wd;
+            const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false), h23 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+            int wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (v0 - h01[0]), 16.0f * (v1 - h01[1]), 0, false);
+            wl = __builtin_amdgcn_cvt_pk_fp8_f32(16.0f * (v2 - h23[0]), 16.0f * (v3 - h23[1]), wl, true);
+            q8l[j][k] = wl;
+          }
+      }
     }
 
     f32x16 o[DB];
@@ -347,15 +403,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // loads in flight.
       const int64_t head_off_b = (int64_t)x.g * D * esz;
       const int rec_bytes = ((1 << shift) - 1) * row_b + D * esz;
-      // DMA rings, and the tiles the MFMAs read (the same for bf16 pools)
+      // DMA rings, and the V tile the PV MFMAs read (the ring's own for bf16 pools)
       auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::DTB; };
       auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::DTB; };
-      auto kcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB : kstage(t); };
-      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB + S::TB : vstage(t); };
-      // fp8: widen one DMA tile into its bf16 tile (swizzled as the bf16 DMA
-      // would have written it); thread tid owns 16 codes: row tid / CH,
+      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB : vstage(t); };
+      // fp8: widen one raw V tile into the bf16 V tile (swizzled as the bf16
+      // DMA would have written it); thread tid owns 16 codes: row tid / CH,
       // columns 16 (tid % CH) .. + 15.  Codes convert exactly (scale 1).
-      auto widen = [&](const uint8_t* raw, uint8_t* bf, bool is_k) {
+      auto widen = [&](const uint8_t* raw, uint8_t* bf) {
         if constexpr (kFp8) {
           const int r = tid / S::CH, cc = tid % S::CH;
           const u32x4 w = *reinterpret_cast<const u32x4*>(raw + r * S::DROWB + 16 * cc);
@@ -365,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             h[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, false));
             h[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, true));
           }
-          const int sw = is_k ? swz_k<D>(r) : swz_v<D>(r);
+          const int sw = swz_v<D>(r);
           uint8_t* row = bf + r * S::ROWB;
           *reinterpret_cast<u32x4*>(row + (((2 * cc) ^ sw) << 4)) = u32x4{h[0], h[1], h[2], h[3]};
           *reinterpret_cast<u32x4*>(row + (((2 * cc + 1) ^ sw) << 4)) = u32x4{h[4], h[5], h[6], h[7]};
@@ -389,13 +444,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           const int r0 = S::RPI * (wave * S::IPW + j);
           const int r = r0 + lane / S::CH;
           const int key = min(t * kKT + r, kmax1);
-          const int cc = kFp8 ? lane % S::CH : (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
+          const int cc = kFp8 ? (is_k ? (lane % S::CH) ^ swz_k8(r) : lane % S::CH)
+                              : (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
           dma16(base, live ? rec_bytes : 0, tile + r0 * S::DROWB, (key & pmask) * row_b + cc * 16);
         }
       };
       // S^T of this wave's key half of K tile t: keys 32 kh + 8 (i / 4) + 4 hf + (i % 4)
       auto qk = [&](int t, f32x16& acc) {
-        const uint8_t* kt = kcomp(t);
+        if constexpr (kFp8) {
+          // fp8 pools: 32x32x64 fp8 MFMAs straight from the raw K tile, K
+          // codes times Q's hi codes, then times its lo codes with the
+          // MFMA's block scale 2^-4 on B (the K and Q scales multiply the
+          // scores later)
+          const int kr = 32 * kh + ln;
+          const uint8_t* row = kstage(t) + kr * S::DROWB;
+          const int sw = swz_k8(kr);
+          acc = f32x16{};
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c0 = 4 * j + 2 * hf;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(row + ((c0 ^ sw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(row + (((c0 + 1) ^ sw) << 4));
+            const i32x8_t a = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[j], acc, 0, 0, 0, 127, 0, 127);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8l[j], acc, 0, 0, 0, 127, 0, 123);
+          }
+          return;
+        }
+        const uint8_t* kt = kstage(t);
         const int kr = 32 * kh + ln;
         u32x4 a[KSTEPS];
 #pragma unroll
@@ -406,8 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         for (int s2 = 0; s2 < KSTEPS; ++s2) acc = mfma32x32x16_bf16(a[s2], q[s2], acc);
         // Keep 4 K operand reads in flight ahead of the MFMA chain.  Left to
         // itself the scheduler (at the register limit) issues each read right
-        // before its MFMA and waits for it.  (The fp8 kernel, with its
-        // widening pass, has no registers to spare for it.)
+        // before its MFMA and waits for it.
         if constexpr (!kFp8) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // 4 LDS reads
 #pragma unroll
@@ -478,10 +554,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       dma_tile(vpool_b, vstage(t0), t0, false);
       dma_tile(kpool_b, kstage(t0 + 2), t0 + 2, true);
       wait_dma_and_barrier<S::IPW>();
-      if constexpr (kFp8) {
-        widen(kstage(t0), kcomp(t0), true);
-        __syncthreads();
-      }
       f32x16 sA, sB;
       u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
       qk(t0, sA);
@@ -494,9 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked) {
         // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight
         if constexpr (kFp8) {
-          widen(kstage(t + 1), kcomp(t + 1), true);
-          asm volatile("" ::: "memory");   // one tile's temporaries at a time
-          widen(vstage(t - 1), vcomp(t - 1), false);
+          widen(vstage(t - 1), vcomp(t - 1));
           __syncthreads();
         }
         if (need_refresh) {
@@ -513,7 +583,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         // lazy rescale: the offset of a row moves only when its max grows by
         // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
         const ScaleCache sct = tile_scales(t);   // tile t's page stays cached across a refresh
-        const float mtc = mt * sct.a;
+        const float sa = sct.a * qsc;   // score multiplier of this tile and row
+        const float mtc = mt * sa;
         const bool grow = mtc > mc + 8.0f;
         if (__any(grow)) {
           const float mc_new = grow ? mtc : mc;
@@ -538,8 +609,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         for (int mu = 0; mu < 2; ++mu)
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            const float e0 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2], sct.a, -mcu));
-            const float e1 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2 + 1], sct.a, -mcu));
+            const float e0 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2], sa, -mcu));
+            const float e1 = fast_exp2(fmaf(s_cur[8 * mu + 2 * q2 + 1], sa, -mcu));
             psum += e0 + e1;
             p_cur[mu][q2] = pack_bf16x2(e0, e1);
           }
@@ -574,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // PV of the last tile (its P is in pB), then drain the trailing
       // zero-range loads before the stages are reused
       if constexpr (kFp8) {
-        widen(vstage(t1 - 1), vcomp(t1 - 1), false);
+        widen(vstage(t1 - 1), vcomp(t1 - 1));
         __syncthreads();
       }
       pv(t1 - 1, pB);

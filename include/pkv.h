@@ -277,7 +277,9 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
  * rows are moved to LDS as they are; QK^T runs on fp8 MFMA from the raw K
  * codes, with q held per row as two e4m3 code sets (about 2^-8 relative,
  * near bf16's own rounding), and PV on bf16 MFMA over V widened exactly in
- * LDS.  The scale of each (page, kv head) is applied in the softmax (K scale
+ * LDS.  The fp8 MFMA accumulates less exactly than fp32 when one product
+ * dominates a 64-dim block (a q row with a 4096x outlier: lse off by up to
+ * 0.33), still inside the fp8 tolerance.  The scale of each (page, kv head) is applied in the softmax (K scale
  * on the scores, V scale on the probabilities and back out of their sum).  Scales
  * must be >= 0; a scale below 2^-100 acts as 2^-100 (so 0 gives keys of
  * score 0 and values of weight ~0, as code x 0 would, without 0 x inf).

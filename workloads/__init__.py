@@ -426,11 +426,13 @@ def make_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, num_q
 
 def make_fp8_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, num_q_heads, num_kv_heads,
                           head_dim, page_size, causal_block_size, num_pool_pages=None, extra_table_cols=1,
-                          zero_scale_pages=0):
+                          zero_scale_pages=0, q_outlier=1.0):
     """Prefill over an fp8 e4m3fn K/V pool: every key, the current block's
     included, is resident (quantised with a scale per (page, kv head)); Q is
     bf16, rows ``seq_len[b] ..`` are padding; dead rows of the last page are
-    NaN codes.  ``zero_scale_pages`` owned pages get K and V scales of 0."""
+    NaN codes.  ``zero_scale_pages`` owned pages get K and V scales of 0.
+    ``q_outlier`` multiplies one dim of every Q row (dim = row % head_dim), so
+    the rest of the row is small next to the row's largest entry."""
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     n_ctxs = np.asarray(n_ctxs, dtype=np.int64)
     totals = n_ctxs + seq_lens
@@ -450,6 +452,9 @@ def make_fp8_prefill_case(name, seed, perm_seed, batch, s_q, seq_lens, n_ctxs, n
         pool.v_scale[pick] = 0.0
     rng = np.random.Generator(np.random.PCG64(seed + 7))
     qkv_f = rng.standard_normal((batch, s_q, num_q_heads + 2 * num_kv_heads, head_dim), dtype=np.float32)
+    if q_outlier != 1.0:
+        rows = np.arange(s_q)
+        qkv_f[:, rows, :num_q_heads, rows % head_dim] *= np.float32(q_outlier)
     slots = np.full(batch * s_q, -1, dtype=np.int64)
     return PrefillCase(name, pool, to_storage(qkv_f, "bf16"), num_q_heads, num_kv_heads, tables,
                        n_ctxs.astype(np.int32), seq_lens.astype(np.int32), causal_block_size,

@@ -521,6 +521,78 @@ __global__ __launch_bounds__(256, 2) void shared_prefix_kernel(DecodeParams pre,
   }
 }
 
+// Head-parallel stream-K worker (units of one 16-row block; kv heads a
+// multiple of 4): a workgroup is one worker whose 4 waves take kv heads
+// 4 hg .. 4 hg + 3 of the same keys.  The flattened positions are (table row
+// t, head quad hg, tile k), cut into equal chunks, one per workgroup; every
+// wave of a workgroup walks the same tiles, so the 4 heads' 256-byte segments
+// of each key row (1 KiB, contiguous) are fetched together, and the other
+// quads of the row are at the same offsets of their own chunks.  Slots: a
+// cut unit's state goes to row 64 (2 w + s) + 16 wave + r of the workspace
+// (s = 0 for the workgroup's first segment, 1 for its last).
+template <int D, bool kFp8>
+__device__ __forceinline__ void decode_sk_heads(const DecodeParams& p, const int32_t* cum, int R) {
+  const int T = p.num_tables;
+  const int HG = p.num_kv_heads >> 2;
+  const int64_t N = (int64_t)cum[T] * HG;
+  const int64_t C = (N + p.n_workers - 1) / p.n_workers;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int r_lane = lane & 15, j = lane >> 4;
+  const int64_t c_begin = (int64_t)worker * C;
+  const int64_t c_end = c_begin + C < N ? c_begin + C : N;
+  if (c_begin >= c_end) return;
+  int t = 0;
+  {
+    int lo = 0, hi = T;   // invariant: cum[lo]*HG <= c_begin < cum[hi]*HG
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)cum[mid] * HG <= c_begin) lo = mid; else hi = mid;
+    }
+    t = lo;
+  }
+  const bool row_ok = r_lane < R;
+  int64_t c = c_begin;
+  while (c < c_end) {
+    const int tiles = cum[t + 1] - cum[t];
+    if (tiles == 0) { ++t; continue; }
+    const int64_t off = c - (int64_t)cum[t] * HG;
+    const int hg = (int)(off / tiles);
+    const int k0 = (int)(off - (int64_t)hg * tiles);
+    const int k1 = (int64_t)tiles < k0 + (c_end - c) ? tiles : (int)(k0 + (c_end - c));
+    const int g = 4 * hg + wave;
+    int qi;
+    int64_t qrow;
+    row_of(p, t, g, row_ok ? r_lane : 0, qi, qrow);
+    u32x4 q[D / 32];
+    load_q<D, kFp8>(q, p, qrow, row_ok);
+    RowState<D> st;
+    reset_state(st);
+    const int len = p.kv_lens[t];
+    walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                        row_limit(p, len, 0), k0, 1, k1 - k0);
+    st.l += __shfl_xor(st.l, 16, 64);
+    st.l += __shfl_xor(st.l, 32, 64);
+    const bool empty = st.l == 0.f;
+    const float inv = empty ? 0.f : 1.0f / st.l;
+    const float lse = empty ? kNegInf : (st.m + fast_log2(st.l)) * kLn2;
+    if (row_ok) {
+      if (k0 == 0 && k1 == tiles) {
+        store_row<D>(st, reinterpret_cast<uint8_t*>(p.out) + qrow * D * (p.out_bf16 ? 2 : 4), p.out_bf16, inv);
+        if (p.out_lse && j == 0) p.out_lse[qrow] = lse;
+      } else {
+        const int slot = 2 * worker + (c == c_begin ? 0 : 1);
+        const int64_t prow = (int64_t)slot * 64 + wave * 16 + r_lane;
+        store_row<D>(st, p.ws_o + prow * D, false, inv);
+        if (j == 0) p.ws_lse[prow] = lse;
+      }
+    }
+    c += k1 - k0;
+    if (hg + 1 == HG) ++t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Stream-K kernel: a persistent grid of workers (WR waves each: the row
 // blocks of one (table row, kv head, row group) unit).  The flattened list of
@@ -564,6 +636,12 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
       for (int i = threadIdx.x; i <= T; i += 256) p.ws_cum[i] = cum[i];
   }
   const int R = p.rows_per_table * p.group;
+  if constexpr (WR == 1) {
+    if (p.head_par) {
+      decode_sk_heads<D, kFp8>(p, cum, R);
+      return;
+    }
+  }
   const int HR = p.num_kv_heads * p.row_groups;   // units per table row
   const int64_t N = (int64_t)cum[T] * HR;
   const int64_t C = (N + p.n_workers - 1) / p.n_workers;
@@ -652,7 +730,13 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_pe
   const int t = (int)(tg / p.num_kv_heads);
   const int rows_w = 16 * wr_per_worker;
   const int rg = r / rows_w;
-  const int HR = p.num_kv_heads * p.row_groups;
+  // head-parallel workers: position space (t, head quad, tile), 64 slot rows
+  // per slot (4 waves x 16); otherwise (t, unit, tile), rows_w rows per slot
+  const bool hp = p.head_par != 0;
+  const int HR = hp ? (p.num_kv_heads >> 2) : p.num_kv_heads * p.row_groups;
+  const int slot_rows = hp ? 64 : rows_w;
+  const int slot_off = hp ? 16 * (g & 3) : 0;
+  const int ux = hp ? (g >> 2) : g * p.row_groups + rg;
   const int T = p.num_tables;
   const int32_t cum_all = p.ws_cum[T], cum_t = p.ws_cum[t], cum_t1 = p.ws_cum[t + 1];
   const int64_t N = (int64_t)cum_all * HR;
@@ -664,13 +748,13 @@ __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_pe
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lse_out = kNegInf;
   if (tiles > 0) {
-    const int64_t F = (int64_t)cum_t * HR + (int64_t)(g * p.row_groups + rg) * tiles;
+    const int64_t F = (int64_t)cum_t * HR + (int64_t)ux * tiles;
     const int64_t w0 = F / C, w1 = (F + tiles - 1) / C;
     if (w0 == w1) return;   // finished by one worker
-    const int row_in = r - rg * rows_w;
+    const int row_in = slot_off + r - rg * rows_w;
     auto slot_row = [&](int64_t w) {
       const int64_t slot = (w == w0) ? (F == w0 * C ? 2 * w0 : 2 * w0 + 1) : 2 * w;
-      return slot * rows_w + row_in;
+      return slot * slot_rows + row_in;
     };
     // one pass (LSE and outputs of PB pieces loaded together); the running
     // sums are rescaled when the running max grows
@@ -863,9 +947,17 @@ static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream)
     per_cu = n;
   }
   const int blocks = per_cu * sm_count;
-  p.n_workers = blocks * (4 / WR);
-  if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
-  const int grid = p.n_workers / (4 / WR);
+  // one 16-row block per unit and kv heads in quads: head-parallel workgroups
+  p.head_par = (WR == 1 && p.row_groups == 1 && p.num_kv_heads % 4 == 0) ? 1 : 0;
+  int grid;
+  if (p.head_par) {
+    grid = blocks < kMaxSkWaves / 4 ? blocks : kMaxSkWaves / 4;
+    p.n_workers = grid;
+  } else {
+    p.n_workers = blocks * (4 / WR);
+    if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
+    grid = p.n_workers / (4 / WR);
+  }
   hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -270,6 +270,7 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   p.out_bf16 = out_dtype == PKV_BF16;
   p.n_workers = 0;
   p.row_groups = sk_rg;
+  p.head_par = 0;
   p.causal = causal;
   p.write_state = 0;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -380,6 +381,7 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
   pre.out_bf16 = 0;
   pre.n_workers = 0;
   pre.row_groups = 0;
+  pre.head_par = 0;
   pre.causal = 0;
   pre.write_state = 1;
   pre.scale_log2 = sm_scale * 1.4426950408889634f;

@@ -67,6 +67,8 @@ struct DecodeParams {
   int32_t out_bf16;
   int32_t n_workers;          // stream-K workers (set by the launcher)
   int32_t row_groups;         // stream-K: row groups per (table row, kv head)
+  int32_t head_par;           // stream-K, one 16-row block per unit: a workgroup's 4 waves take
+                              // 4 kv heads of the same keys (set by the launcher)
   int32_t causal;             // rows of a table row are a step's tokens: row i sees len - (n - 1 - i) keys
   int32_t write_state;        // always leave the normalised state of split s in ws_o / ws_lse (empty too)
   float scale_log2;           // sm_scale * log2(e)

@@ -605,14 +605,25 @@ __device__ __forceinline__ void decode_sk_heads(const DecodeParams& p, const int
 // depend only on the lengths, never on page ids, so results are independent
 // of where pages sit in the pool.
 // ---------------------------------------------------------------------------
-template <int D, bool kFp8, int WR>
-__global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
-  constexpr int WPW = 4 / WR;   // workers per workgroup
-  __shared__ int32_t cum[kMaxSkTables + 1];
-  __shared__ int32_t part[256];
+// Prefix sums of the tiles per table row, cum[0..T], from kv_lens (every
+// workgroup; ends with a barrier); workgroup 0 also leaves them in ws_cum for
+// the merge.  Up to 64 rows: one wave's shuffle scan.
+__device__ __forceinline__ void sk_prefix_sums(const DecodeParams& p, int32_t* cum, int32_t* part) {
   const int T = p.num_tables;
-  // ---- prefix sums of tiles per table row (every workgroup, from kv_lens)
-  {
+  if (T <= 64) {
+    if (threadIdx.x < 64) {
+      const int i = threadIdx.x;
+      int v = i < T ? (p.kv_lens[i] + 31) >> 5 : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off, 64);
+        if (i >= off) v += u;
+      }
+      if (i < T) cum[i + 1] = v;
+      if (i == 0) cum[0] = 0;
+    }
+    __syncthreads();
+  } else {
     const int per = (T + 255) / 256;
     const int lo = threadIdx.x * per;
     int run = 0;
@@ -632,16 +643,28 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
     }
     if (threadIdx.x == 255) cum[T] = part[255];
     __syncthreads();
-    if (blockIdx.x == 0)
-      for (int i = threadIdx.x; i <= T; i += 256) p.ws_cum[i] = cum[i];
   }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= T; i += 256) p.ws_cum[i] = cum[i];
+}
+
+// Head-parallel stream-K kernel (see decode_sk_heads).
+template <int D, bool kFp8>
+__global__ __launch_bounds__(256, 2) void decode_skh_kernel(DecodeParams p) {
+  __shared__ int32_t cum[kMaxSkTables + 1];
+  __shared__ int32_t part[256];
+  sk_prefix_sums(p, cum, part);
+  decode_sk_heads<D, kFp8>(p, cum, p.rows_per_table * p.group);
+}
+
+template <int D, bool kFp8, int WR>
+__global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
+  constexpr int WPW = 4 / WR;   // workers per workgroup
+  __shared__ int32_t cum[kMaxSkTables + 1];
+  __shared__ int32_t part[256];
+  const int T = p.num_tables;
+  sk_prefix_sums(p, cum, part);
   const int R = p.rows_per_table * p.group;
-  if constexpr (WR == 1) {
-    if (p.head_par) {
-      decode_sk_heads<D, kFp8>(p, cum, R);
-      return;
-    }
-  }
   const int HR = p.num_kv_heads * p.row_groups;   // units per table row
   const int64_t N = (int64_t)cum[T] * HR;
   const int64_t C = (N + p.n_workers - 1) / p.n_workers;
@@ -711,11 +734,11 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
 // Joins the partial states of units cut by chunk boundaries, and writes the
 // zero output / -inf LSE of table rows with no keys.  One thread per (row,
 // 4 dims) of every unit; units a single worker finished are skipped.  The
-// loads of each stage go out together (prefix sums, then the pieces' LSEs,
-// then LSEs and values, 4 pieces at a time), so a merge costs three memory
+// loads of each stage go out together (prefix sums, then LSEs and values of
+// up to 8 pieces at a time), so a merge of up to 8 pieces costs two memory
 // round trips rather than one per piece.
 __global__ __launch_bounds__(256) void merge_sk_kernel(DecodeParams p, int wr_per_worker, int head_dim) {
-  constexpr int PB = 4;
+  constexpr int PB = 8;
   const int D = head_dim;
   const int chunks = D >> 2;
   const int R = p.rows_per_table * p.group;
@@ -937,28 +960,29 @@ int sk_waves_per_worker(int rows_per_unit) {
 template <int D, bool kFp8, int WR>
 static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream) {
   // a persistent grid: as many workgroups as stay resident at once
-  static int resident[2] = {0, 0};   // per-kernel occupancy, queried once
-  int& per_cu = resident[0];
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0) != hipSuccess ||
-        n < 1)
-      n = 1;
-    per_cu = n;
-  }
-  const int blocks = per_cu * sm_count;
   // one 16-row block per unit and kv heads in quads: head-parallel workgroups
   p.head_par = (WR == 1 && p.row_groups == 1 && p.num_kv_heads % 4 == 0) ? 1 : 0;
+  static int resident[2] = {0, 0};   // per-kernel occupancy, queried once
+  int& per_cu = resident[p.head_par];
+  if (per_cu == 0) {
+    int n = 0;
+    const hipError_t q = p.head_par
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_skh_kernel<D, kFp8>, 256, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0);
+    per_cu = (q != hipSuccess || n < 1) ? 1 : n;
+  }
+  const int blocks = per_cu * sm_count;
   int grid;
   if (p.head_par) {
     grid = blocks < kMaxSkWaves / 4 ? blocks : kMaxSkWaves / 4;
     p.n_workers = grid;
+    hipLaunchKernelGGL((decode_skh_kernel<D, kFp8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
     p.n_workers = blocks * (4 / WR);
     if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
     grid = p.n_workers / (4 / WR);
+    hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
   }
-  hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int R = p.rows_per_table * p.group;

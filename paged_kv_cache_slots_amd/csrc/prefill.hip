@@ -735,11 +735,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 // in slot 2 w' + 1 when it is not the first segment of that chunk.  Thread
 // (g, lane) owns values 16 g .. 16 g + 15 of the slot rows of row block rb
 // and lane, so each load instruction reads 256 contiguous bytes; piece loads
-// go out 4 at a time.  (One workgroup per row block rather than per unit:
+// go out 8 at a time.  (One workgroup per row block rather than per unit:
 // the merge is bound by load latency, so it wants many small workgroups.)
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillParams p, int main_grid) {
-  constexpr int PB = 4;   // pieces per batch of loads
+  constexpr int PB = 8;   // pieces per batch of loads
   __shared__ int32_t tcum[kMaxTailUnits + 1];
   const int xcd = blockIdx.x & 7;
   const int k = (blockIdx.x >> 3) % kMaxTailUnits;

@@ -170,14 +170,16 @@ def test_decode_parity(case, use_ws):
     check_decode(c, use_ws=use_ws)
 
 
-def test_decode_stream_k_many_rows_with_empty_ones():
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (24, 12)], ids=["per-unit", "head-quads2", "head-quads3"])
+def test_decode_stream_k_many_rows_with_empty_ones(hq, hkv):
     """Hundreds of table rows (some empty) so that chunk boundaries cut many
-    units and whole units fall inside one worker's chunk."""
+    units and whole units fall inside one worker's chunk; with kv heads in
+    quads the workers are head-parallel workgroups (2 or 3 quads per row)."""
     rng = np.random.default_rng(3)
     lens = rng.integers(0, 300, size=300)
     lens[::7] = 0
     lens[5] = 4000
-    c = W.make_decode_case("many_rows", 81, 1081, len(lens), 8, 2, 128, 32, lens, new_per_seq=1)
+    c = W.make_decode_case("many_rows", 81, 1081, len(lens), hq, hkv, 128, 32, lens, new_per_seq=1)
     check_decode(c, use_ws="sk")
     check_decode(c, out_dtype=torch.float32, use_ws="sk")
 

@@ -349,6 +349,91 @@ __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D /
   }
 }
 
+// The same walk for the four waves of a workgroup that own different row
+// blocks of one unit (bf16, D = 128): every wave needs the whole K/V tile, so
+// each tile goes from HBM to registers to LDS once.  Wave w loads register
+// slots 4 w .. 4 w + 3 of every lane (slots 0-7: the 16-byte K chunks of
+// half 0 then half 1; 8-15: the V rows of half 0 then half 1), writes them to
+// an LDS stage in that register image, and every wave reads the whole image
+// back, so compute_tile sees exactly what its own loads would have returned.
+// Two LDS stages, two tiles in flight per wave (a quarter tile each), one
+// barrier per tile.  All four waves must call it with the same arguments.
+template <int D>
+__device__ __forceinline__ void walk_tiles_shared(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
+                                                  const int32_t* trow, int g, int len, int lim, int lim_lo,
+                                                  int first, int step, int n) {
+  static_assert(D == 128, "the shared walk stages bf16 tiles of 128 dims");
+  using T = TileRegs<D, false>;
+  static_assert(T::KLD == 4 && T::VB == 16, "16 register slots of 16 bytes per lane");
+  __shared__ u32x4 stage[2][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r_lane = lane & 15, j = lane >> 4;
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k_pool);
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.v_pool);
+  const int64_t page_stride_b = p.page_stride * 2;
+  const int64_t head_off_b = (int64_t)g * D * 2;
+  const int row_b = p.num_kv_heads * D * 2;
+  const int page_bytes = (1 << p.page_shift) * row_b;
+  const int pmask = (1 << p.page_shift) - 1;
+  const LaneOffsets lo{r_lane * row_b + 16 * j, 4 * j * row_b + (D / 16) * r_lane * 2};
+  const int te = first + (n - 1) * step + 1;
+  // this wave's quarter of tile k of the window: wave 0 / 1 the K chunks of
+  // half 0 / 1, wave 2 / 3 the V rows of half 0 / 1
+  const bool is_k = wave < 2;
+  const bool half1 = (wave & 1) != 0;
+  auto issue = [&](u32x4 (&x)[4], const PageWindow& win, int w0, int k, int n_win) {
+    const bool ok = k < n_win;
+    const int kc = ok ? k : 0;
+    const int key0 = (first + (w0 + kc) * step) * 32;
+    const int page = half1 ? rl(win.e1, kc) : rl(win.e0, kc);
+    const int row = ((half1 ? key0 + 16 : key0) & pmask);
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(is_k ? kp : vp, page, page_stride_b, head_off_b, ok ? page_bytes : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = is_k ? __builtin_amdgcn_raw_buffer_load_b128(rs, lo.k + 64 * i, row * row_b, 0)
+                  : __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v, (row + i) * row_b, 0);
+  };
+  auto put = [&](int b, const u32x4 (&x)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[b][4 * wave + i][lane] = x[i];
+  };
+  auto get = [&](int b, T& r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r.k[h][c] = stage[b][4 * h + c][lane];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 v = stage[b][8 + t][lane];
+      r.v[t][0] = v[0]; r.v[t][1] = v[1]; r.v[t][2] = v[2]; r.v[t][3] = v[3];
+    }
+  };
+  T r;
+  for (int w0 = 0; w0 < n; w0 += 64) {
+    const PageWindow win = fetch_pages<false>(p, trow, g, first + w0 * step, step, te, len);
+    const int n_win = n - w0 < 64 ? n - w0 : 64;
+    u32x4 xa[4], xb[4];
+    issue(xa, win, w0, 0, n_win);
+    issue(xb, win, w0, 1, n_win);
+    put(0, xa);
+    __syncthreads();
+    for (int k = 0; k < n_win; k += 2) {
+      issue(xa, win, w0, k + 2, n_win);
+      get(0, r);
+      compute_tile<D, false>(st, r, q, p.scale_log2, (first + (w0 + k) * step) * 32, len, lim, lim_lo);
+      put(1, xb);
+      __syncthreads();
+      if (k + 1 >= n_win) break;
+      issue(xb, win, w0, k + 3, n_win);
+      get(1, r);
+      compute_tile<D, false>(st, r, q, p.scale_log2, (first + (w0 + k + 1) * step) * 32, len, lim, lim_lo);
+      put(0, xa);
+      __syncthreads();
+    }
+  }
+}
+
 // Store the normalised rows of a finished state: lane (r, j) holds dims
 // DPL*(4j+i) + t' of row r.  `dst` points at the row's D outputs.
 template <int D>
@@ -426,9 +511,16 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   reset_state(st);
   const int first = tb + wp;
   const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
-  if (rb * 16 < R && n_mine > 0)
-    walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                        row_limit(p, len, 0), first, WP, n_mine);
+  if constexpr (WP == 1 && D == 128 && !kFp8) {
+    // four row blocks of one unit: every wave walks (the workgroup shares each tile through LDS)
+    if (n_mine > 0)
+      walk_tiles_shared<D>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                           row_limit(p, len, 0), first, 1, n_mine);
+  } else {
+    if (rb * 16 < R && n_mine > 0)
+      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                          row_limit(p, len, 0), first, WP, n_mine);
+  }
 
   st.l += __shfl_xor(st.l, 16, 64);
   st.l += __shfl_xor(st.l, 32, 64);
@@ -707,9 +799,15 @@ __global__ __launch_bounds__(256, 2) void decode_sk_kernel(DecodeParams p) {
     RowState<D> st;
     reset_state(st);
     const int len = p.kv_lens[t];
-    if (rb * 16 < R)
-      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                          row_limit(p, len, 0), k0, 1, k1 - k0);
+    if constexpr (WR == 4 && D == 128 && !kFp8) {
+      // one worker = the workgroup's four row blocks of one unit: every wave walks the segment
+      walk_tiles_shared<D>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                           row_limit(p, len, 0), k0, 1, k1 - k0);
+    } else {
+      if (rb * 16 < R)
+        walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
+                            row_limit(p, len, 0), k0, 1, k1 - k0);
+    }
     st.l += __shfl_xor(st.l, 16, 64);
     st.l += __shfl_xor(st.l, 32, 64);
     const bool empty = st.l == 0.f;

@@ -27,6 +27,15 @@ static_assert(kMaxCausalBlocks == PKV_MAX_CAUSAL_BLOCKS, "block limit of the ABI
 #endif
 constexpr int kMinSplitTokens = PKV_MIN_SPLIT_TOKENS;
 constexpr int kMaxSplits = PKV_MAX_SPLITS;
+// Prefix splits of the fused n-sample step.  Its prefix workgroups share each
+// tile through LDS across the four row blocks of the group, which makes a
+// tile cheap next to a workgroup's start-up and the extra state every split
+// adds to the merge; measured on the n-sample workload (2048-token prefixes),
+// splits of at least 1024 keys beat the split decode's 512.
+#ifndef PKV_SHARED_MIN_SPLIT_TOKENS
+#define PKV_SHARED_MIN_SPLIT_TOKENS 1024
+#endif
+constexpr int kSharedMinSplitTokens = PKV_SHARED_MIN_SPLIT_TOKENS;
 
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3FN; }
 int elem_bytes(pkv_dtype d) { return d == PKV_F32 ? 4 : d == PKV_BF16 ? 2 : 1; }
@@ -55,9 +64,9 @@ struct SplitPlan {
   int tiles_per_split;
 };
 
-SplitPlan plan_decode(int32_t max_kv_len) {
+SplitPlan plan_decode(int32_t max_kv_len, int min_split_tokens = kMinSplitTokens) {
   const int64_t tiles = std::max<int64_t>(1, ceil_div(std::max(max_kv_len, 0), 32));
-  const int64_t by_len = ceil_div(std::max(max_kv_len, 1), kMinSplitTokens);
+  const int64_t by_len = ceil_div(std::max(max_kv_len, 1), min_split_tokens);
   const int splits = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, by_len));
   return SplitPlan{splits, (int)ceil_div(tiles, splits)};
 }
@@ -311,7 +320,7 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
 size_t pkv_attn_decode_shared_prefix_workspace_bytes(int32_t groups, int32_t samples, int32_t q_len,
                                                      int32_t num_q_heads, int32_t head_dim, int32_t max_prefix_len) {
   if (groups < 0 || samples < 1 || q_len < 1 || num_q_heads < 1 || head_dim < 1 || max_prefix_len < 0) return 0;
-  const int64_t states = plan_decode(max_prefix_len).splits + 1;
+  const int64_t states = plan_decode(max_prefix_len, kSharedMinSplitTokens).splits + 1;
   const int64_t rows = (int64_t)groups * samples * q_len;
   return (size_t)(states * rows * num_q_heads * (int64_t)(head_dim + 1) * (int64_t)sizeof(float));
 }
@@ -349,7 +358,7 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
                                                                     max_prefix_len);
   if (workspace_bytes < need) return PKV_ERR_SHAPE;
 
-  const SplitPlan plan = plan_decode(max_prefix_len);
+  const SplitPlan plan = plan_decode(max_prefix_len, kSharedMinSplitTokens);
   const int64_t rows = (int64_t)groups * samples * q_len;
   const int64_t plane = rows * num_q_heads;
   float* ws_o = static_cast<float*>(workspace);

@@ -29,8 +29,9 @@
 //     an 8-key x (D/16)-dim block that each lane loads directly (a 16-lane
 //     group reads whole 256-byte rows) and transposes with v_perm_b32.  The
 //     output row of a lane is its softmax row, so rescaling needs no shuffle.
-//   * fp8: codes are widened to bf16 exactly (v_cvt_pk_f32_fp8; an e4m3
-//     value fits bf16), the per-(page, kv head) K scale multiplies the scores
+//   * fp8: codes are widened to bf16 exactly, two per instruction
+//     (v_cvt_scalef32_pk_bf16_fp8 with scale 1; an e4m3 value fits bf16),
+//     the per-(page, kv head) K scale multiplies the scores
 //     and the V scale is folded into P before the PV product.
 //   * Dead rows of a partial last page and poison pages are selected away
 //     (scores to -inf, V rows to 0) before they can reach a product.
@@ -172,10 +173,8 @@ __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>&
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
           const uint32_t dw = raw[2 * e + w];
-          const f32x2 f0 = fp8x2_to_f32<false>(dw);
-          const f32x2 f1 = fp8x2_to_f32<true>(dw);
-          a[2 * w] = pack_hi16(__float_as_uint(f0[0]), __float_as_uint(f0[1]));
-          a[2 * w + 1] = pack_hi16(__float_as_uint(f1[0]), __float_as_uint(f1[1]));
+          a[2 * w] = fp8x2_to_bf16x2<false>(dw);
+          a[2 * w + 1] = fp8x2_to_bf16x2<true>(dw);
         }
       } else {
         a = r.k[h][i];
@@ -269,10 +268,8 @@ __device__ __forceinline__ void compute_tile(RowState<D>& st, TileRegs<D, kFp8>&
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
         const uint32_t mixed = perm_b32(r.v[2 * q2 + 1][w], r.v[2 * q2][w], sel);
-        const f32x2 lo = fp8x2_to_f32<false>(mixed);
-        const f32x2 hi = fp8x2_to_f32<true>(mixed);
-        a0[q2] = pack_hi16(__float_as_uint(lo[0]), __float_as_uint(lo[1]));
-        a1[q2] = pack_hi16(__float_as_uint(hi[0]), __float_as_uint(hi[1]));
+        a0[q2] = fp8x2_to_bf16x2<false>(mixed);
+        a1[q2] = fp8x2_to_bf16x2<true>(mixed);
       }
       st.o[tp] = mfma16x16x32_bf16(a0, pb, st.o[tp]);
       st.o[tp + 1] = mfma16x16x32_bf16(a1, pb, st.o[tp + 1]);

@@ -46,6 +46,14 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t packed) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(packed, kHiWord);
 }
 
+// Two e4m3fn codes (byte pair `word` of `packed`) -> two bf16 in one dword,
+// low half from the lower byte.  Every e4m3 value is a bf16 value, so with
+// scale 1 the conversion is exact (checked over all 65536 code pairs).
+template <bool kHiWord>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)packed, 1.0f, kHiWord));
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                   0, 0, 0);

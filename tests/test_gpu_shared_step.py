@@ -67,9 +67,11 @@ def test_shared_step_parity(case):
     check_shared(c)
 
 
-def test_shared_step_workload_shape_fp32_out():
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32_out", "bf16_out"])
+def test_shared_step_workload_shape(out_dtype):
     """The n-sample workload: 8 prompts x 16 samples, 2048 shared keys, tails
-    U[1, 512], 32/8 heads x 128, one new token per sample."""
+    U[1, 512], 32/8 heads x 128, one new token per sample (bf16 output is the
+    benchmarked form)."""
     tl = np.random.default_rng(4).integers(1, 512, size=128, endpoint=True)
     c = W.make_shared_step_case("workload", 52, 1052, 8, 16, 1, [2048] * 8, tl, 32, 8, 128, 32)
-    check_shared(c, torch.float32)
+    check_shared(c, out_dtype)

@@ -188,9 +188,22 @@ def run_headline(args, torch, pkv, W):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the scatter's own latency, in steps of its own (outside the timed loop:
+    # an extra event inside it would lengthen every step)
+    sev = []
+    for _ in range(20):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        pkv.pkv_scatter_slots(dev["pool"], dev["new_k"], dev["new_v"], dev["slots"])
+        s1.record()
+        sev.append((s0, s1))
+        pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], case.max_kv_len, case.sm_scale,
+                            dev["out"], None, dev["ws"])
+    torch.cuda.synchronize()
+    scat_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
     flushed = time_events(torch, lambda: step(), 20, Flusher(torch))
     return case, dict(step_bytes=step_bytes, dec_bytes=dec_bytes, ms_per_step=wall * 1e3, decode_ms=dec_ms,
-                      flushed_step_ms=flushed)
+                      scatter_ms=scat_ms, scatter_bytes=scat_bytes, flushed_step_ms=flushed)
 
 
 # ----------------------------------------------------------------------------- secondary workloads
@@ -573,6 +586,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "pkv_attn_decode call (decode kernel + split merge kernel)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
+        "scatter": {"what": "the step's pkv_scatter_slots of 64 new tokens (latency-bound at this size)",
+                    "ms": round(h["scatter_ms"], 5), "bytes": h["scatter_bytes"]},
         "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],
         "device": device_info(torch, pkv),
         "copy_ceiling": copy_ceiling(torch),

@@ -184,6 +184,33 @@ def test_decode_stream_k_many_rows_with_empty_ones(hq, hkv):
     check_decode(c, out_dtype=torch.float32, use_ws="sk")
 
 
+def _random_decode_case(seed):
+    """A seeded random decode shape: pool dtype, head_dim, page size, GQA
+    grouping (kv heads 1-12), rows per table 1-4 and lengths 0-1500 (some
+    empty), so that head-parallel and per-unit stream-K workers, cut and whole
+    units and every page-size path occur across the seeds."""
+    rng = np.random.default_rng(900 + seed)
+    kv = "fp8" if rng.random() < 0.3 else "bf16"
+    d = 128 if (kv == "fp8" or rng.random() < 0.7) else 64
+    ps = int(rng.choice([32, 64])) if kv == "fp8" else int(rng.choice([16, 32, 64]))
+    hkv = int(rng.choice([1, 2, 4, 8, 12]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    n = int(rng.integers(1, 5))
+    t = int(rng.integers(1, 40))
+    lens = rng.integers(0, 1500, size=t)
+    lens[rng.random(t) < 0.1] = 0
+    lens[0] = max(int(lens[0]), 1)
+    return W.make_decode_case(f"rand{seed}", 700 + seed, 1700 + seed, t, hkv * group, hkv, d, ps, lens,
+                              kv_dtype=kv, rows_per_table=n, new_per_seq=0 if kv == "fp8" else 1,
+                              extra_table_cols=1, num_pool_pages=sum(math.ceil(int(L) / ps) for L in lens) + 5)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_random_shapes(seed):
+    c = _random_decode_case(seed)
+    check_decode(c, use_ws=["sk", "split", "none"][seed % 3])
+
+
 def test_decode_fp32_out_and_fp32_query_paths():
     lens = [3, 64, 129, 700]
     c = W.make_decode_case("f32out", 41, 1041, len(lens), 8, 2, 128, 32, lens, kv_dtype="bf16", new_per_seq=1)

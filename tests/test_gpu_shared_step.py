@@ -67,6 +67,31 @@ def test_shared_step_parity(case):
     check_shared(c)
 
 
+def _random_shared_case(seed):
+    """A seeded random n-sample step: groups, samples and step tokens, prefix
+    lengths from empty to several splits, tails shorter and longer than the
+    step, bf16 (128 or 64 dims) or fp8 pools and GQA groupings, so the prefix
+    runs both as LDS-shared four-row-block workgroups and as the other forms."""
+    rng = np.random.default_rng(500 + seed)
+    kv = "fp8" if rng.random() < 0.3 else "bf16"
+    d = 128 if (kv == "fp8" or rng.random() < 0.75) else 64
+    ps = 32 if kv == "fp8" else int(rng.choice([16, 32]))
+    hkv = int(rng.choice([2, 4, 8]))
+    group = int(rng.choice([1, 2, 4]))
+    groups = int(rng.integers(1, 4))
+    samples = int(rng.integers(1, 17))
+    n = int(rng.integers(1, 5))
+    pl = rng.integers(0, 3000, size=groups)
+    tl = rng.integers(1, 400, size=groups * samples)
+    return W.make_shared_step_case(f"rand{seed}", 600 + seed, 1600 + seed, groups, samples, n, pl, tl,
+                                   hkv * group, hkv, d, ps, kv_dtype=kv)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shared_step_random_shapes(seed):
+    check_shared(_random_shared_case(seed))
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["fp32_out", "bf16_out"])
 def test_shared_step_workload_shape(out_dtype):
     """The n-sample workload: 8 prompts x 16 samples, 2048 shared keys, tails

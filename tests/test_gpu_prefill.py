@@ -98,6 +98,32 @@ def test_prefill_small_exhaustive(case, use_ws):
     check(c, use_ws=use_ws)
 
 
+def _random_prefill_case(seed):
+    """A seeded random block-causal prefill: batch 1-3 with its own context and
+    real-token counts (padding and empty entries included), causal block sizes
+    from one token to the whole batch entry, GQA groupings, 64 or 128 dims and
+    page sizes 16-64."""
+    rng = np.random.default_rng(800 + seed)
+    b = int(rng.integers(1, 4))
+    s_q = int(rng.integers(20, 300))
+    seqs = [int(x) for x in rng.integers(0, s_q + 1, size=b)]
+    seqs[0] = max(seqs[0], 1)
+    ctxs = [int(x) for x in rng.integers(0, 900, size=b)]
+    hkv = int(rng.choice([1, 2, 3]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    ps = int(rng.choice([16, 32, 64]))
+    cbs = int(rng.choice([0, 1, 17, 64, s_q]))
+    return W.make_prefill_case(f"rand{seed}", 300 + seed, 1300 + seed, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs,
+                               num_pool_pages=sum(math.ceil((x + y) / ps) for x, y in zip(seqs, ctxs)) + 5,
+                               extra_table_cols=2)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_shapes(seed):
+    check(_random_prefill_case(seed), use_ws=seed % 2 == 0)
+
+
 def test_prefill_fp32_output():
     c = W.make_prefill_case("f32out", 92, 1092, 1, 140, [133], [50], 4, 2, 128, 32, 20, extra_table_cols=1)
     check(c, out_dtype=torch.float32)

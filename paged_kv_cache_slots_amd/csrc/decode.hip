@@ -1065,6 +1065,10 @@ static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream)
         ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_skh_kernel<D, kFp8>, 256, 0)
         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0);
     per_cu = (q != hipSuccess || n < 1) ? 1 : n;
+    // A worker of four row blocks (64-row units) streams each tile once for
+    // all four; one such workgroup per CU halves the cut pieces and start-ups
+    // per unit (measured 3 % faster on the n-sample prefix pass than two).
+    if (WR == 4) per_cu = 1;
   }
   const int blocks = per_cu * sm_count;
   int grid;

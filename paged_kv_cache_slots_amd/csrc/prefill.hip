@@ -735,8 +735,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 }
 
 // Merge of the split leftover units: workgroup (rb, k, xcd) of a grid of
-// 4 x kMaxTailUnits x 8 combines, for row block rb, the pieces of leftover
-// unit k of XCD xcd with the log-sum-exp merge, in key order.  The piece of
+// 4 x tail_units x 8 (tail_units: the largest leftover count of any XCD)
+// combines, for row block rb, the pieces of leftover unit k of XCD xcd with
+// the log-sum-exp merge, in key order.  The piece of
 // chunk w sits in slot 2 w' of the main kernel's workgroup w' = xcd + 8 w, or
 // in slot 2 w' + 1 when it is not the first segment of that chunk.  Thread
 // (g, lane) owns values 16 g .. 16 g + 15 of the slot rows of row block rb
@@ -744,12 +745,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 // go out 8 at a time.  (One workgroup per row block rather than per unit:
 // the merge is bound by load latency, so it wants many small workgroups.)
 template <int D>
-__global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillParams p, int main_grid) {
+__global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillParams p, int main_grid, int tail_units) {
   constexpr int PB = 8;   // pieces per batch of loads
   __shared__ int32_t tcum[kMaxTailUnits + 1];
   const int xcd = blockIdx.x & 7;
-  const int k = (blockIdx.x >> 3) % kMaxTailUnits;
-  const int rb = (blockIdx.x >> 3) / kMaxTailUnits;
+  const int k = (blockIdx.x >> 3) % tail_units;
+  const int rb = (blockIdx.x >> 3) / tail_units;
   const int Gx = main_grid >> 3;
   const XcdPlan plan = xcd_plan(p, xcd, Gx);
   if (!plan.sk || k >= plan.nt) return;
@@ -844,18 +845,20 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
   // merge only when some XCD splits its leftover units (the same test as the kernels')
   const int64_t kv_units = (int64_t)p.batch * p.num_kv_heads;
   const int64_t per_kv = (int64_t)p.group * p.q_tiles;
+  // (the grid covers the largest leftover count of any XCD)
   const int gx = g / 8;
-  bool any = false;
+  int tail_units = 0;
   for (int xcd = 0; xcd < 8; ++xcd) {
     const int64_t nkv = kv_units > xcd ? (kv_units - xcd + 7) / 8 : 0;
     const int64_t r = (nkv * per_kv) % gx;
-    any = any || (r != 0 && r <= kMaxTailUnits);
+    if (r != 0 && r <= kMaxTailUnits && r > tail_units) tail_units = (int)r;
   }
-  if (!any) return e;
+  if (tail_units == 0) return e;
+  const dim3 mgrid((unsigned)(4 * 8 * tail_units));
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3(4 * 8 * kMaxTailUnits), dim3(256), 0, stream, p, g);
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, mgrid, dim3(256), 0, stream, p, g, tail_units);
   else
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3(4 * 8 * kMaxTailUnits), dim3(128), 0, stream, p, g);
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, mgrid, dim3(128), 0, stream, p, g, tail_units);
   return hipGetLastError();
 }
 

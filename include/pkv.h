@@ -218,8 +218,8 @@ pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q
  *   workspace     device scratch of at least
  *                 pkv_attn_decode_shared_prefix_workspace_bytes(...) bytes,
  *                 16-byte aligned, contents ignored: the fp32 states of the
- *                 prefix's key splits (>= 512 keys each, <= 16) and of the
- *                 tails.  Two calls in flight need two workspaces.
+ *                 prefix's key splits (>= 1024 keys each, <= 16) and of
+ *                 the tails.  Two calls in flight need two workspaces.
  * Kernels: one launch of every prefix-split and tail workgroup (bf16 MFMA;
  * K/V bf16 or fp8 e4m3fn; head_dim 64 or 128; page_size >= 16), then one
  * merge launch.

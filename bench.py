@@ -182,11 +182,18 @@ def run_headline(args, torch, pkv, W):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed steps: wall clock only (HIP events between the launches would
+    # lengthen every step, by ~5 us for the pair around the decode call)
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # the decode call's own duration: the same number of steps again, with HIP
+    # events on the launch stream around every call
     for _ in range(args.steps):
         step(record=True)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     # the scatter's own latency, in steps of its own (outside the timed loop:
     # an extra event inside it would lengthen every step)
@@ -585,6 +592,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "pkv_attn_decode call (decode kernel + split merge kernel)",
+                     "timing": "HIP events around each call over --steps further steps (not inside the wall-clock "
+                               "loop, where they lengthen every step)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
         "scatter": {"what": "the step's pkv_scatter_slots of 64 new tokens (latency-bound at this size)",
                     "ms": round(h["scatter_ms"], 5), "bytes": h["scatter_bytes"]},

@@ -1054,37 +1054,31 @@ int sk_waves_per_worker(int rows_per_unit) {
 
 template <int D, bool kFp8, int WR>
 static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream) {
-  // a persistent grid: as many workgroups as stay resident at once
   // one 16-row block per unit and kv heads in quads: head-parallel workgroups
   p.head_par = (WR == 1 && p.row_groups == 1 && p.num_kv_heads % 4 == 0) ? 1 : 0;
-  static int resident[2] = {0, 0};   // per-kernel occupancy, queried once
-  int& per_cu = resident[p.head_par];
-  if (per_cu == 0) {
-    int n = 0;
-    const hipError_t q = p.head_par
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_skh_kernel<D, kFp8>, 256, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0);
-    per_cu = (q != hipSuccess || n < 1) ? 1 : n;
-    // A worker of four row blocks (64-row units) streams each tile once for
-    // all four; one such workgroup per CU halves the cut pieces and start-ups
-    // per unit (measured 3 % faster on the n-sample prefix pass than two).
-    if (WR == 4) per_cu = 1;
-  }
-  int blocks = per_cu * sm_count;
-  // Short work (fewer than 16 tiles per workgroup even at the host's length
-  // bound): one head-parallel workgroup per CU, so that each walks longer
-  // chunks with fewer cut pieces (the n-sample tails: 0.0824 -> 0.0803 ms for
-  // the unfused step; long decodes keep two).
-  if (p.head_par && blocks > sm_count &&
-      (int64_t)p.num_tables * p.tiles_per_split * (p.num_kv_heads / 4) < 16 * (int64_t)blocks)
-    blocks = sm_count;
   int grid;
   if (p.head_par) {
-    grid = blocks < kMaxSkWaves / 4 ? blocks : kMaxSkWaves / 4;
+    // One head-parallel workgroup per CU.  With two per CU the first-resident
+    // one wins issue and ends early while the other runs on alone, so one per
+    // CU loses no bandwidth and walks chunks twice as long, with half the cut
+    // pieces and start-ups (GQA call 0.1223 -> 0.1195 ms, long fp8 0.849 ->
+    // 0.844 ms; 192 workgroups ran the same, 320 and 384 slower).
+    grid = sm_count < kMaxSkWaves / 4 ? sm_count : kMaxSkWaves / 4;
     p.n_workers = grid;
     hipLaunchKernelGGL((decode_skh_kernel<D, kFp8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
-    p.n_workers = blocks * (4 / WR);
+    // a persistent grid: as many workgroups as stay resident at once
+    static int resident = 0;   // occupancy, queried once
+    if (resident == 0) {
+      int n = 0;
+      const hipError_t q = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0);
+      resident = (q != hipSuccess || n < 1) ? 1 : n;
+    }
+    // A worker of four row blocks (64-row units) streams each tile once for
+    // all four; one such workgroup per CU halves the cut pieces and start-ups
+    // per unit (measured 3 % faster on the n-sample prefix pass than two).
+    const int per_cu = WR == 4 ? 1 : resident;
+    p.n_workers = per_cu * sm_count * (4 / WR);
     if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
     grid = p.n_workers / (4 / WR);
     hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);

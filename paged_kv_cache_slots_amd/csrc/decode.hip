@@ -1056,31 +1056,19 @@ template <int D, bool kFp8, int WR>
 static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream) {
   // one 16-row block per unit and kv heads in quads: head-parallel workgroups
   p.head_par = (WR == 1 && p.row_groups == 1 && p.num_kv_heads % 4 == 0) ? 1 : 0;
-  int grid;
+  // One workgroup per CU.  With two per CU the first-resident one wins issue
+  // and ends early while the other runs on alone, so one per CU loses no
+  // bandwidth and walks chunks twice as long, with half the cut pieces and
+  // start-ups.  Measured against two per CU: GQA call 0.1223 -> 0.1195 ms,
+  // long fp8 decode 0.849 -> 0.844 ms, n-sample prefix (64-row units) and
+  // tails 3 % each, 16 q / 2 kv heads 0.0390 -> 0.0359 ms; 192 workgroups ran
+  // the same as 256, 128, 320 and 384 slower.
+  const int grid = sm_count < kMaxSkWaves / 4 ? sm_count : kMaxSkWaves / 4;
   if (p.head_par) {
-    // One head-parallel workgroup per CU.  With two per CU the first-resident
-    // one wins issue and ends early while the other runs on alone, so one per
-    // CU loses no bandwidth and walks chunks twice as long, with half the cut
-    // pieces and start-ups (GQA call 0.1223 -> 0.1195 ms, long fp8 0.849 ->
-    // 0.844 ms; 192 workgroups ran the same, 320 and 384 slower).
-    grid = sm_count < kMaxSkWaves / 4 ? sm_count : kMaxSkWaves / 4;
     p.n_workers = grid;
     hipLaunchKernelGGL((decode_skh_kernel<D, kFp8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
-    // a persistent grid: as many workgroups as stay resident at once
-    static int resident = 0;   // occupancy, queried once
-    if (resident == 0) {
-      int n = 0;
-      const hipError_t q = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_sk_kernel<D, kFp8, WR>, 256, 0);
-      resident = (q != hipSuccess || n < 1) ? 1 : n;
-    }
-    // A worker of four row blocks (64-row units) streams each tile once for
-    // all four; one such workgroup per CU halves the cut pieces and start-ups
-    // per unit (measured 3 % faster on the n-sample prefix pass than two).
-    const int per_cu = WR == 4 ? 1 : resident;
-    p.n_workers = per_cu * sm_count * (4 / WR);
-    if (p.n_workers > kMaxSkWaves / WR) p.n_workers = kMaxSkWaves / WR;
-    grid = p.n_workers / (4 / WR);
+    p.n_workers = grid * (4 / WR);
     hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();

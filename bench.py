@@ -17,7 +17,9 @@ launch stream with a 512 MiB read between steps (outside the events) so
 their working sets cannot stay in the 256 MiB Infinity Cache.
 
 ``roofline`` describes the dominant call of the headline (the decode), timed
-with HIP events around each call inside the timed region; ``cpu_baseline``
+with HIP events on the launch stream around each call of a second run of
+``--steps`` steps after the timed region (events inside it would add their own
+cost to the wall-clock step); ``cpu_baseline``
 times the float64 CPU oracle (single thread) on a bounded sample of the same
 headline batch.
 """
@@ -111,6 +113,15 @@ def decode_bytes(kv_lens, page_size, hkv, d, kv_esize, n_rows_q, hq, q_esize, ou
         b += n_rows_q * hq * 4
     b += int(pages.sum()) * 4 + len(kv_lens) * 4
     return b
+
+
+def prefill_flops(seq_len, n_ctx, causal_block_size, d, hq):
+    """Algorithmic flops of one batch entry of the block-causal prefill: QK^T
+    and PV, 2 flops per multiply-add each, over the keys every real query
+    sees (n_ctx + the end of its causal block; padding rows count nothing)."""
+    cbs = causal_block_size or seq_len
+    vis = sum(n_ctx + min((i // cbs + 1) * cbs, seq_len) for i in range(seq_len))
+    return 4.0 * d * hq * vis
 
 
 class Flusher:
@@ -247,9 +258,7 @@ def run_prefill(torch, pkv, W, flush):
     for _ in range(5):
         prefill()
     seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
-    cbs = case.causal_block_size or seq_len
-    vis = sum(ctx + min((i // cbs + 1) * cbs, seq_len) for i in range(seq_len))
-    flops = 4.0 * d * hq * vis
+    flops = prefill_flops(seq_len, ctx, case.causal_block_size, d, hq)
     med, p10, p90 = time_events(torch, prefill, 30, flush)
     smed, _, _ = time_events(torch, scatter, 30, flush)
     both, _, _ = time_events(torch, lambda: (scatter(), prefill()), 30, flush)
@@ -289,7 +298,7 @@ def run_fp8_prefill(torch, pkv, W, flush):
     for _ in range(5):
         prefill()
     seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
-    flops = 4.0 * d * hq * sum(ctx + seq_len for _ in range(seq_len))
+    flops = prefill_flops(seq_len, ctx, case.causal_block_size, d, hq)
     med, p10, p90 = time_events(torch, prefill, 30, flush)
     tflops = flops / (med * 1e-3) / 1e12
     # half the flops (QK^T) run on fp8 MFMA, half (PV) on bf16 MFMA: at both peaks

@@ -572,9 +572,11 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
 // Split kernel: grid (split, kv head, table row x row group).
 template <int D, bool kFp8, int WP>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeParams p) {
-  const int n_rg = gridDim.z / p.num_tables;
-  const int t = blockIdx.z / n_rg;
-  decode_block<D, kFp8, WP>(p, blockIdx.x, blockIdx.y, t, blockIdx.z - t * n_rg);
+  // grid (tables x row groups, kv heads, splits): the table count takes the
+  // x dimension, the only one not capped at 65535 blocks
+  const int n_rg = gridDim.x / p.num_tables;
+  const int t = blockIdx.x / n_rg;
+  decode_block<D, kFp8, WP>(p, blockIdx.z, blockIdx.y, t, blockIdx.x - t * n_rg);
 }
 
 // Row blocks of 16 rows and waves per row block for R rows (as the split
@@ -932,8 +934,8 @@ __device__ __forceinline__ float load_kv(const void* pool, int64_t idx) {
 template <int D, int QT, int KV>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   constexpr int DPT = D / 64;   // dims per lane in the PV product
-  const int s = blockIdx.x;
-  const int64_t qrow = blockIdx.y;   // (t * n + i) * Hq + h
+  const int s = blockIdx.y;
+  const int64_t qrow = blockIdx.x;   // (t * n + i) * Hq + h; x: not capped at 65535 blocks
   const int h = (int)(qrow % p.num_q_heads);
   const int t = (int)(qrow / ((int64_t)p.num_q_heads * p.rows_per_table));
   const int g = h / p.group;
@@ -1029,14 +1031,14 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   const int blocks16 = (R + 15) / 16;
   const dim3 block(256);
   if (blocks16 <= 1) {
-    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables);
+    const dim3 grid(p.num_tables, p.num_kv_heads, p.splits);
     hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 4>), grid, block, 0, stream, p);
   } else if (blocks16 <= 2) {
-    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables);
+    const dim3 grid(p.num_tables, p.num_kv_heads, p.splits);
     hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 2>), grid, block, 0, stream, p);
   } else {
     const int rg = (blocks16 + 3) / 4;
-    const dim3 grid(p.splits, p.num_kv_heads, p.num_tables * rg);
+    const dim3 grid(p.num_tables * rg, p.num_kv_heads, p.splits);
     hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 1>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
@@ -1128,7 +1130,7 @@ hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, in
 
 template <int D, int QT>
 static hipError_t launch_valu_dq(const DecodeParams& p, ElemType kv, hipStream_t stream) {
-  const dim3 grid(p.splits, (unsigned)((int64_t)p.num_tables * p.rows_per_table * p.num_q_heads)), block(64);
+  const dim3 grid((unsigned)((int64_t)p.num_tables * p.rows_per_table * p.num_q_heads), p.splits), block(64);
   if (kv == kF32) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kF32>), grid, block, 0, stream, p);
   else if (kv == kBF16) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kBF16>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((decode_valu_kernel<D, QT, kFP8>), grid, block, 0, stream, p);

@@ -274,3 +274,43 @@ def test_full_size_long_fp8_decode_sampled():
     rng = np.random.default_rng(1)
     subset = sorted(set(rng.choice(len(c.kv_lens), 5, replace=False).tolist()) | {int(np.argmax(c.kv_lens))})
     check_decode(c, subset=subset)
+
+
+@pytest.mark.parametrize("tables", [8192, 8193], ids=["stream_k_limit", "past_limit_split_path"])
+def test_decode_table_count_at_and_past_the_stream_k_limit(tables):
+    """8192 table rows is the most the stream-K kernel takes (its prefix sums
+    of tiles per row live in LDS); one more row falls back to the key-split
+    kernel with the same workspace.  Short and empty rows; sampled rows are
+    checked, among them the first, the last and the longest."""
+    rng = np.random.default_rng(tables)
+    lens = rng.integers(0, 80, size=tables)
+    lens[::11] = 0
+    lens[tables // 2] = 700
+    c = W.make_decode_case(f"tables{tables}", 83, 1083, tables, 8, 2, 64, 32, lens, new_per_seq=1)
+    subset = sorted(set(rng.choice(tables, 12, replace=False).tolist()) | {0, tables - 1, tables // 2})
+    check_decode(c, use_ws="sk", subset=subset)
+
+
+def test_decode_fp32_query_rows_past_65535_blocks():
+    """The fp32 kernel runs one workgroup per (query row, q head) and split:
+    2100 tables x 32 q heads = 67,200 of them, more than a grid's y or z
+    dimension holds, with one long row so the keys are split."""
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 40, size=2100)
+    lens[::13] = 0
+    lens[1234] = 3000
+    c = W.make_decode_case("fp32_many_rows", 84, 1084, len(lens), 32, 4, 64, 16, lens, kv_dtype="f32",
+                           new_per_seq=1)
+    subset = sorted(set(rng.choice(len(lens), 10, replace=False).tolist()) | {0, 1234, len(lens) - 1})
+    check_decode(c, out_dtype=torch.float32, use_ws="split", subset=subset)
+
+
+def test_decode_more_tables_than_65535_without_workspace():
+    """Without a workspace the bf16 decode runs one workgroup per table row and
+    kv head: 65,600 table rows take more blocks than a grid's y or z dimension
+    holds."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(1, 17, size=65600)
+    c = W.make_decode_case("bf16_many_tables", 85, 1085, len(lens), 2, 1, 64, 16, lens, new_per_seq=1)
+    subset = sorted(set(rng.choice(len(lens), 10, replace=False).tolist()) | {0, 65535, len(lens) - 1})
+    check_decode(c, use_ws="none", subset=subset)

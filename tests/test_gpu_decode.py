@@ -314,3 +314,15 @@ def test_decode_more_tables_than_65535_without_workspace():
     c = W.make_decode_case("bf16_many_tables", 85, 1085, len(lens), 2, 1, 64, 16, lens, new_per_seq=1)
     subset = sorted(set(rng.choice(len(lens), 10, replace=False).tolist()) | {0, 65535, len(lens) - 1})
     check_decode(c, use_ws="none", subset=subset)
+
+
+def test_headline_decode_is_run_to_run_bit_identical():
+    """Stream-K cut points depend only on the lengths and the CU count, and
+    every partial state is merged in a fixed order, so two calls on the same
+    inputs give the same bits (outputs and LSE)."""
+    c = W.gqa_bf16_decode()
+    note("gqa_bf16_decode twice, bitwise")
+    out1, lse1, _ = run_decode(c)
+    out2, lse2, _ = run_decode(c)
+    assert np.array_equal(out1.view(np.uint64), out2.view(np.uint64))
+    assert np.array_equal(lse1.view(np.uint64), lse2.view(np.uint64))

@@ -20,8 +20,16 @@ their working sets cannot stay in the 256 MiB Infinity Cache.
 with HIP events on the launch stream around each call of a second run of
 ``--steps`` steps after the timed region (events inside it would add their own
 cost to the wall-clock step); ``cpu_baseline``
-times the float64 CPU oracle (single thread) on a bounded sample of the same
-headline batch.
+times the float64 CPU oracle on whole steps of the same headline batch.
+
+Every timed workload is first checked against the float64 oracle on its own
+output (the whole output, every row), within the tolerances the path is held
+to (bf16: 2e-2 abs + 2e-2 rel on outputs; fp8 K/V: 6e-2 + 6e-2; LSE 2e-2 /
+6e-2 absolute; integer and byte results bit-exact).  A workload that fails is
+reported with its error and no figures; a failing headline prints no value and
+exits with status 1.  Each workload entry carries ``parity_max_err``, the
+oracle's own seconds on that workload (``oracle_s``) and the host cores it was
+given (``cores``: BLAS threads = the process's CPU affinity).
 """
 
 from __future__ import annotations
@@ -39,6 +47,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ORACLE_CORES = len(os.sched_getaffinity(0))   # BLAS threads given to the oracle
+# output tolerances |gpu - ref| <= atol + rtol |ref|, and the absolute LSE bound
+OUT_TOL = {"bf16": (2e-2, 2e-2), "fp8": (6e-2, 6e-2)}
+LSE_TOL = {"bf16": 2e-2, "fp8": 6e-2}
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8
 
@@ -59,7 +71,7 @@ def parse():
     ap.add_argument("--workloads", default="prefill,fp8prefill,shared,fp8,commit",
                     help="secondary workloads to run: comma list of prefill, fp8prefill, shared, fp8, commit (or none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (calibrates the HBM byte counters) and exit")
     return ap.parse_args()
@@ -91,6 +103,60 @@ def recorded_traffic():
         return int(kv["traffic_bytes_per_call"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+class ParityError(RuntimeError):
+    pass
+
+
+def oracle_threads():
+    """Context in which numpy's BLAS uses every core of this process's affinity."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=ORACLE_CORES)
+
+
+def bf16_to_f64(t):
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return (t.view(torch.int16).numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+            np.float64)
+    return t.numpy().astype(np.float64)
+
+
+def check_out(got, ref, tol, what):
+    """Max |got - ref| after checking every element against the tolerance."""
+    atol, rtol = OUT_TOL[tol]
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.shape != ref.shape:
+        raise ParityError(f"{what}: shape {got.shape} != {ref.shape}")
+    if not np.all(np.isfinite(got)):
+        raise ParityError(f"{what}: non-finite values in the GPU output")
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    if np.any(bad):
+        raise ParityError(f"{what}: {int(bad.sum())} of {err.size} values outside tolerance (max err "
+                          f"{err.max():.3g})")
+    return float(err.max()) if err.size else 0.0
+
+
+def check_lse(got, ref, tol, what):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    inf = np.isinf(ref)
+    if not (np.array_equal(np.isinf(got), inf) and np.array_equal(got[inf], ref[inf])):
+        raise ParityError(f"{what}: infinities differ")
+    err = np.abs(got[~inf] - ref[~inf])
+    if err.size and (np.isnan(err).any() or err.max() > LSE_TOL[tol]):
+        raise ParityError(f"{what}: LSE off by {np.nanmax(err):.3g} > {LSE_TOL[tol]}")
+    return float(err.max()) if err.size else 0.0
+
+
+def timed_oracle(fn):
+    """Run an oracle computation on every core; returns (result, seconds)."""
+    with oracle_threads():
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
 
 
 def to_dev(a, torch):
@@ -190,6 +256,20 @@ def run_headline(args, torch, pkv, W):
             b.record()
             ev.append((a, b))
 
+    # parity gate: the first step's output against the oracle (whole batch)
+    import oracle as orc
+    step()
+    torch.cuda.synchronize()
+    got = bf16_to_f64(dev["out"])
+
+    def ref_step():
+        kp = orc.scatter_slots(case.pool.k, case.new_k, case.slots)
+        vp = orc.scatter_slots(case.pool.v, case.new_v, case.slots)
+        return orc.attn_decode(kp, vp, case.q, case.tables, case.kv_lens, case.sm_scale)
+
+    (ref, _), oracle_s = timed_oracle(ref_step)
+    parity = {"parity_max_err": check_out(got, ref, "bf16", "headline decode"), "oracle_s": round(oracle_s, 3),
+              "cores": ORACLE_CORES, "parity_rows": int(ref.shape[0] * ref.shape[1] * ref.shape[2])}
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -221,7 +301,7 @@ def run_headline(args, torch, pkv, W):
     scat_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
     flushed = time_events(torch, lambda: step(), 20, Flusher(torch))
     return case, dict(step_bytes=step_bytes, dec_bytes=dec_bytes, ms_per_step=wall * 1e3, decode_ms=dec_ms,
-                      scatter_ms=scat_ms, scatter_bytes=scat_bytes, flushed_step_ms=flushed)
+                      scatter_ms=scat_ms, scatter_bytes=scat_bytes, flushed_step_ms=flushed, parity=parity)
 
 
 # ----------------------------------------------------------------------------- secondary workloads
@@ -253,12 +333,36 @@ def run_prefill(torch, pkv, W, flush):
         scatter()
         prefill()
         torch.cuda.synchronize()
+        got = bf16_to_f64(out)
+        lse = torch.empty((1, s_q, hq), dtype=torch.float32, device="cuda:0")
+        pkv.pkv_attn_prefill_block_causal(pool, q, tables, n_ctx, seq, case.causal_block_size, case.max_keys,
+                                          case.sm_scale, out, lse, ws)
+        torch.cuda.synchronize()
+        got_lse = lse.cpu().numpy()
     except pkv.PkvError as e:
         return {"error": str(e)}
+    import oracle as orc
+
+    def ref_step():
+        k_np, v_np = case.qkv.reshape(s_q, hq + 2 * hkv, d)[:, hq:hq + hkv], case.qkv.reshape(
+            s_q, hq + 2 * hkv, d)[:, hq + hkv:]
+        kp = orc.scatter_slots(case.pool.k, k_np, case.slots)
+        vp = orc.scatter_slots(case.pool.v, v_np, case.slots)
+        return orc.attn_prefill_block_causal(kp, vp, case.qkv[:, :, :hq], case.tables, case.n_ctx, case.seq_len,
+                                             case.causal_block_size, case.sm_scale)
+
+    (ref, ref_lse), oracle_s = timed_oracle(ref_step)
+    try:
+        parity = {"parity_max_err": check_out(got, ref, "bf16", "prefill out"),
+                  "parity_max_lse_err": check_lse(got_lse, ref_lse, "bf16", "prefill lse"),
+                  "oracle_s": round(oracle_s, 3), "cores": ORACLE_CORES}
+    except ParityError as e:
+        return {"error": f"parity failed: {e}"}
     for _ in range(5):
         prefill()
     seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
     flops = prefill_flops(seq_len, ctx, case.causal_block_size, d, hq)
+    parity["oracle_gflops"] = round(flops / oracle_s / 1e9, 2)
     med, p10, p90 = time_events(torch, prefill, 30, flush)
     smed, _, _ = time_events(torch, scatter, 30, flush)
     both, _, _ = time_events(torch, lambda: (scatter(), prefill()), 30, flush)
@@ -268,7 +372,7 @@ def run_prefill(torch, pkv, W, flush):
                         "prefix + 4096 history + own block, 32-token pages",
             "gflop": flops / 1e9, "prefill_ms": med, "prefill_ms_p10_p90": [p10, p90], "tflops": tflops,
             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS, "scatter_ms": smed,
-            "scatter_gbs": scat_bytes / (smed * 1e-3) / 1e9, "scatter_plus_prefill_ms": both}
+            "scatter_gbs": scat_bytes / (smed * 1e-3) / 1e9, "scatter_plus_prefill_ms": both, **parity}
 
 
 def run_fp8_prefill(torch, pkv, W, flush):
@@ -293,12 +397,30 @@ def run_fp8_prefill(torch, pkv, W, flush):
     try:
         prefill()
         torch.cuda.synchronize()
+        got = bf16_to_f64(out)
+        lse = torch.empty((1, s_q, hq), dtype=torch.float32, device="cuda:0")
+        pkv.pkv_attn_prefill_block_causal(pool, q, tables, n_ctx, seq, case.causal_block_size, case.max_keys,
+                                          case.sm_scale, out, lse, ws)
+        torch.cuda.synchronize()
+        got_lse = lse.cpu().numpy()
     except pkv.PkvError as e:
         return {"error": str(e)}
+    import oracle as orc
+    (ref, ref_lse), oracle_s = timed_oracle(lambda: orc.attn_prefill_block_causal(
+        case.pool.k, case.pool.v, case.qkv[:, :, :hq], case.tables, case.n_ctx, case.seq_len,
+        case.causal_block_size, case.sm_scale, kv_dtype="fp8", q_dtype="bf16", k_scale=case.pool.k_scale,
+        v_scale=case.pool.v_scale))
+    try:
+        parity = {"parity_max_err": check_out(got, ref, "fp8", "fp8 prefill out"),
+                  "parity_max_lse_err": check_lse(got_lse, ref_lse, "fp8", "fp8 prefill lse"),
+                  "oracle_s": round(oracle_s, 3), "cores": ORACLE_CORES}
+    except ParityError as e:
+        return {"error": f"parity failed: {e}"}
     for _ in range(5):
         prefill()
     seq_len, ctx = int(case.seq_len[0]), int(case.n_ctx[0])
     flops = prefill_flops(seq_len, ctx, case.causal_block_size, d, hq)
+    parity["oracle_gflops"] = round(flops / oracle_s / 1e9, 2)
     med, p10, p90 = time_events(torch, prefill, 30, flush)
     tflops = flops / (med * 1e-3) / 1e12
     # half the flops (QK^T) run on fp8 MFMA, half (PV) on bf16 MFMA: at both peaks
@@ -309,7 +431,7 @@ def run_fp8_prefill(torch, pkv, W, flush):
                         "(Q as hi + lo e4m3 codes), PV on bf16 MFMA over V widened in LDS",
             "gflop": flops / 1e9, "prefill_ms": med, "prefill_ms_p10_p90": [p10, p90], "tflops": tflops,
             "frac_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS,
-            "frac_mixed_mfma_peak": tflops / mixed_peak}
+            "frac_mixed_mfma_peak": tflops / mixed_peak, **parity}
 
 
 def run_shared_prefix(torch, pkv, W, flush):
@@ -354,6 +476,28 @@ def run_shared_prefix(torch, pkv, W, flush):
         pkv.pkv_scatter_slots(pool, new_k, new_v, slots)
         pkv.pkv_attn_decode_shared_prefix(pool, q, s, pt, plen, mp, tt, tlen, mt, c.sm_scale, fout, ws3)
 
+    # parity gate: the merged, unshared and fused outputs of one step each
+    # against the oracle's attention over the full (prefix + tail) tables
+    import oracle as orc
+    shared()
+    unshared()
+    fused()
+    torch.cuda.synchronize()
+    got_m, got_u, got_f = bf16_to_f64(out), bf16_to_f64(uout)[:, 0], bf16_to_f64(fout)[:, 0]
+
+    def ref_step():
+        kp = orc.scatter_slots(c.pool.k, c.new_k, c.slots)
+        vp = orc.scatter_slots(c.pool.v, c.new_v, c.slots)
+        return orc.attn_decode(kp, vp, c.q, c.full_tables, c.full_lens, c.sm_scale)
+
+    (ref, _), oracle_s = timed_oracle(ref_step)
+    try:
+        parity = {"parity_max_err": max(check_out(got_m, ref[:, 0], "bf16", "prefix + tail + merge"),
+                                        check_out(got_u, ref[:, 0], "bf16", "unshared decode"),
+                                        check_out(got_f, ref[:, 0], "bf16", "fused n-sample step")),
+                  "oracle_s": round(oracle_s, 3), "cores": ORACLE_CORES}
+    except ParityError as e:
+        return {"error": f"parity failed: {e}"}
     for _ in range(5):
         shared()
         unshared()
@@ -374,7 +518,8 @@ def run_shared_prefix(torch, pkv, W, flush):
             "fused_step_ms": fmed, "fused_step_ms_p10_p90": [fp10, fp90],
             "fused_gbs": total / (fmed * 1e-3) / 1e9, "fused_frac_hbm_peak": total / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "fused_launches": 3, "unfused_launches": 6, "unshared_step_ms": umed,
-            "unshared_mb": (decode_bytes(c.full_lens, 32, hkv, d, 2, n_rows, hq, 2, 2, False, False) + scat) / 1e6}
+            "unshared_mb": (decode_bytes(c.full_lens, 32, hkv, d, 2, n_rows, hq, 2, 2, False, False) + scat) / 1e6,
+            "oracle_gbs": round(total / oracle_s / 1e9, 3), **parity}
 
 
 def run_long_fp8(torch, pkv, W, flush):
@@ -387,15 +532,30 @@ def run_long_fp8(torch, pkv, W, flush):
         pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], c.max_kv_len, c.sm_scale,
                             dev["out"], None, dev["ws"])
 
+    # parity gate: every row against the oracle (which streams one sequence
+    # at a time, so host memory stays bounded)
+    import oracle as orc
+    step()
+    torch.cuda.synchronize()
+    got = bf16_to_f64(dev["out"])
+    (ref, _), oracle_s = timed_oracle(lambda: orc.attn_decode(
+        c.pool.k, c.pool.v, c.q, c.tables, c.kv_lens, c.sm_scale, kv_dtype="fp8", q_dtype="bf16",
+        k_scale=c.pool.k_scale, v_scale=c.pool.v_scale))
+    try:
+        parity = {"parity_max_err": check_out(got, ref, "fp8", "fp8 decode"), "oracle_s": round(oracle_s, 3),
+                  "cores": ORACLE_CORES}
+    except ParityError as e:
+        return {"error": f"parity failed: {e}"}
     for _ in range(3):
         step()
     med, p10, p90 = time_events(torch, step, 20, flush)
     nbytes = decode_bytes(c.kv_lens, 32, hkv, d, 1, t * n, hq, 2, 2, False, True)
+    parity["oracle_gbs"] = round(nbytes / oracle_s / 1e9, 3)
     gbs = nbytes / (med * 1e-3) / 1e9
     return {"workload": "fp8 decode: 256 sequences, lengths log-uniform in [1024, 32768], 64/8 heads x 128, "
                         "e4m3fn K/V with per-(page, kv head) scales, bf16 q/out",
             "algorithmic_gb": nbytes / 1e9, "decode_ms": med, "decode_ms_p10_p90": [p10, p90], "gbs": gbs,
-            "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, **parity}
 
 
 def commit_sequence(torch, pkv, flush):
@@ -436,6 +596,45 @@ def commit_sequence(torch, pkv, flush):
         pkv.pkv_scatter_slots(pool, new_k, new_v, lay.stage_slots, slots2=lay.stage_slots2)
         pkv.pkv_copy_slots(pool, lay.current_src, lay.current_dst)
 
+    # parity gate on the first commit and forward: the rotated table, every
+    # layout tensor and the copied pool rows bit-exact against the oracle
+    import oracle as orc
+
+    def host(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+    table0, priv0, k0, v0 = host(table), host(priv), host(k), host(v)
+    commit()
+    torch.cuda.synchronize()
+    fp = b["fixed_pages"]
+    t0 = time.perf_counter()
+    with oracle_threads():
+        want_table = table0.copy()
+        want_table[fp:] = orc.rotate_rows(table0[None, fp:], shift)[0]
+        want = orc.causal_layout(want_table, priv0, ps, pin, window, committed, evicted, sizes, b["table_width"],
+                                 b["list_stride"])
+        ok = np.array_equal(host(table), want_table)
+        for name in ("block_tables", "n_ctx", "seq_len", "stage_slots", "stage_slots2", "commit_src", "commit_dst",
+                     "current_src", "current_dst"):
+            ok = ok and np.array_equal(host(getattr(lay, name)), want[name])
+        k1 = orc.copy_slots(k0, want["commit_src"], want["commit_dst"])
+        v1 = orc.copy_slots(v0, want["commit_src"], want["commit_dst"])
+        ok = ok and np.array_equal(host(k), k1) and np.array_equal(host(v), v1)
+        oracle_s = time.perf_counter() - t0
+    forward_writes()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with oracle_threads():
+        # one layer: scatter of the staged tokens to one or two slots, then the current copies
+        k_l = orc.scatter_slots(k1[0], host(new_k), want["stage_slots"], slots2=want["stage_slots2"])
+        v_l = orc.scatter_slots(v1[0], host(new_v), want["stage_slots"], slots2=want["stage_slots2"])
+        k_l = orc.copy_slots(k_l[None], want["current_src"], want["current_dst"])[0]
+        v_l = orc.copy_slots(v_l[None], want["current_src"], want["current_dst"])[0]
+        ok = ok and np.array_equal(host(k[0]), k_l) and np.array_equal(host(v[0]), v_l)
+        oracle_s += time.perf_counter() - t0
+    del k0, v0, k1, v1, k_l, v_l
+    if not ok:
+        raise ParityError("exact-window commit or forward writes differ from the oracle")
     for _ in range(3):
         commit()
         forward_writes()
@@ -445,7 +644,8 @@ def commit_sequence(torch, pkv, flush):
     n_current = int((lay.current_src >= 0).sum())
     return {"commit_ms": cmed, "commit_ms_p10_p90": [cp10, cp90], "commit_copied_keys": n_commit,
             "forward_writes_ms": fmed, "forward_writes_ms_p10_p90": [fp10, fp90],
-            "forward_current_copied_keys": n_current, "launches_per_commit": 3, "launches_per_forward_layer": 2}
+            "forward_current_copied_keys": n_current, "launches_per_commit": 3, "launches_per_forward_layer": 2,
+            "parity": "bit-exact", "oracle_s": round(oracle_s, 3), "cores": ORACLE_CORES}
 
 
 def run_commit(torch, pkv, W, flush):
@@ -466,6 +666,19 @@ def run_commit(torch, pkv, W, flush):
     def copy():
         pkv.pkv_copy_slots(pool, src, dst, layers, layer_stride)
 
+    import oracle as orc
+
+    def host(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    k0, v0 = host(k), host(v)
+    copy()
+    torch.cuda.synchronize()
+    (k1, v1), oracle_s = timed_oracle(lambda: (orc.copy_slots(k0, src.cpu().numpy(), dst.cpu().numpy()),
+                                               orc.copy_slots(v0, src.cpu().numpy(), dst.cpu().numpy())))
+    if not (np.array_equal(host(k), k1) and np.array_equal(host(v), v1)):
+        return {"error": "parity failed: slot copy differs from the oracle"}
+    del k0, v0, k1, v1
     for _ in range(3):
         copy()
     med, p10, p90 = time_events(torch, copy, 30, flush)
@@ -475,27 +688,32 @@ def run_commit(torch, pkv, W, flush):
     def rot():
         pkv.pkv_rotate_rows(table, 32)
 
+    rot()
+    if not np.array_equal(table.cpu().numpy(), orc.rotate_rows(np.arange(209, dtype=np.int32)[None], 32)[0]):
+        return {"error": "parity failed: row rotation differs from the oracle"}
     for _ in range(3):
         rot()
     rmed, _, _ = time_events(torch, rot, 30, flush)
-    seq = commit_sequence(torch, pkv, flush)
+    try:
+        seq = commit_sequence(torch, pkv, flush)
+    except ParityError as e:
+        return {"error": f"parity failed: {e}"}
     return {"workload": "exact-window commit: private-page fill of 2048 slots x 8 layers (24 kv heads x 128, bf16, "
                         "32-token pages) and the rotation of a 209-page table row",
             "commit_sequence": seq,
             "copy_slots_mb": nbytes / 1e6, "copy_slots_ms": med, "copy_slots_ms_p10_p90": [p10, p90],
             "copy_slots_gbs": nbytes / (med * 1e-3) / 1e9, "copy_slots_frac_hbm_peak": nbytes / (med * 1e-3) / 1e9 /
-            HBM_PEAK_GBS, "rotate_rows_ms": rmed}
+            HBM_PEAK_GBS, "rotate_rows_ms": rmed, "parity": "bit-exact", "oracle_s": round(oracle_s, 3),
+            "cores": ORACLE_CORES}
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(case, seconds):
-    """Time the float64 oracle (one BLAS thread) on whole headline steps
-    (scatter of the new tokens + decode of all 64 sequences), repeated until
-    about ``seconds`` of CPU work; report the same algorithmic bytes per
-    second as the GPU figure."""
-    from threadpoolctl import threadpool_limits
-
+    """Time the float64 oracle on whole headline steps (scatter of the new
+    tokens + decode of all 64 sequences), with numpy's BLAS on every core of
+    this process's affinity, repeated until about ``seconds`` of work; report
+    the same algorithmic bytes per second as the GPU figure."""
     import oracle as orc
 
     hkv, d = case.pool.num_kv_heads, case.pool.head_dim
@@ -503,7 +721,7 @@ def cpu_baseline(case, seconds):
     step_bytes = (decode_bytes(case.kv_lens, case.pool.page_size, hkv, d, 2, t_rows * n, hq, 2, 2, False, False)
                   + 2 * 2 * len(case.slots) * hkv * d * 2 + len(case.slots) * 8)
     steps, spent = 0, 0.0
-    with threadpool_limits(limits=1):
+    with oracle_threads():
         while spent < seconds:
             t0 = time.perf_counter()
             kp = orc.scatter_slots(case.pool.k, case.new_k, case.slots)
@@ -511,10 +729,11 @@ def cpu_baseline(case, seconds):
             orc.attn_decode(kp, vp, case.q, case.tables, case.kv_lens, case.sm_scale)
             spent += time.perf_counter() - t0
             steps += 1
-    return {"value": steps * step_bytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": steps * step_bytes / spent / 1e9, "unit": "GB/s", "cores": ORACLE_CORES, "kind": "oracle",
             "sample": f"{steps} whole steps of the headline batch (scatter of 64 new tokens + float64 decode of "
                       f"all 64 sequences, {int(case.kv_lens.sum())} keys, {step_bytes / 1e6:.1f} MB algorithmic "
-                      f"per step) in {spent:.1f} s on one thread"}
+                      f"per step) in {spent:.1f} s, numpy BLAS on {ORACLE_CORES} threads (the process's CPU "
+                      f"affinity)"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -585,7 +804,13 @@ def main():
         print(json.dumps({"copy_probe_mib": args.copy_probe, "median_ms": float(np.median(ms)),
                           "gbs_read_plus_write": 2 * (args.copy_probe << 20) / (float(np.median(ms)) * 1e-3) / 1e9}))
         return
-    case, h = run_headline(args, torch, pkv, W)
+    try:
+        case, h = run_headline(args, torch, pkv, W)
+    except ParityError as e:
+        # no figure for an output that does not match the oracle
+        print(json.dumps({"metric": "paged decode K/V GB/s (% HBM peak) + block-causal prefill TFLOP/s (% MFMA)",
+                          "value": None, "error": f"headline parity failed: {e}"}))
+        sys.exit(1)
     value = h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9
     achieved = h["dec_bytes"] / (h["decode_ms"] * 1e-3) / 1e9
     result = {
@@ -604,6 +829,7 @@ def main():
                      "timing": "HIP events around each call over --steps further steps (not inside the wall-clock "
                                "loop, where they lengthen every step)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_ms"], 5)},
+        "parity": h["parity"],
         "scatter": {"what": "the step's pkv_scatter_slots of 64 new tokens (latency-bound at this size)",
                     "ms": round(h["scatter_ms"], 5), "bytes": h["scatter_bytes"]},
         "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],

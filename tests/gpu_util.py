@@ -13,8 +13,13 @@ import paged_kv_cache_slots_amd as pkv
 
 DEV = "cuda:0"
 
-# Tolerances: |gpu - ref| <= atol + rtol * |ref| (torch allclose convention).
+# Tolerances of attention outputs: |gpu - ref| <= atol + rtol * |ref| (torch
+# allclose convention).
 TOL = {"f32": (1e-5, 0.0), "bf16": (2e-2, 2e-2), "fp8": (6e-2, 6e-2)}
+# The LSE is a log-domain value: an absolute error e scales every merge weight
+# built from it by exp(e), whatever the LSE's size, so it is held to the
+# absolute part of the tolerance alone (no term that grows with |lse|).
+LSE_ATOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
 
 
 def note(msg: str) -> None:
@@ -66,4 +71,22 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -
         i = int(np.argmax(err - bound))
         raise AssertionError(f"{what}: {int(bad.sum())} of {err.size} outside tolerance; worst |{g[i]} - {r[i]}| "
                              f"= {err[i]:.3g} > {bound[i]:.3g}")
+    return float(err.max()) if err.size else 0.0
+
+
+def assert_lse_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
+    """|lse_gpu - lse_ref| <= LSE_ATOL[dtype] elementwise; -inf (empty key
+    sets, padding rows) must match exactly."""
+    atol = LSE_ATOL[dtype]
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    inf = np.isinf(ref)
+    assert np.array_equal(np.isinf(got), inf) and np.array_equal(got[inf], ref[inf]), f"{what}: infinities differ"
+    assert not np.any(np.isnan(got)), f"{what}: NaN in GPU LSE"
+    err = np.abs(got[~inf] - ref[~inf])
+    if err.size and err.max() > atol:
+        i = int(np.argmax(err))
+        raise AssertionError(f"{what}: {int((err > atol).sum())} of {err.size} LSE values off by more than {atol}; "
+                             f"worst |{got[~inf][i]} - {ref[~inf][i]}| = {err[i]:.3g}")
     return float(err.max()) if err.size else 0.0

@@ -47,3 +47,27 @@ def test_prefill_flops_visibility():
     assert bench.prefill_flops(1560, 5120, 1560, 128, 24) == 128050790400
     # causal_block_size 0 means one block over the whole chunk.
     assert bench.prefill_flops(50, 3, 0, 64, 2) == bench.prefill_flops(50, 3, 50, 64, 2)
+
+
+def test_parity_gate_accepts_within_and_rejects_outside_tolerance():
+    """The bench's gate: outputs within atol + rtol |ref| pass and report the
+    largest error; one element past it, a NaN or a shape mismatch fails; LSE is
+    held to an absolute bound and -inf must match exactly."""
+    import pytest
+    ref = np.linspace(-3, 3, 50)
+    got = ref + 0.5 * (2e-2 + 2e-2 * np.abs(ref))
+    assert abs(bench.check_out(got, ref, "bf16", "x") - np.max(np.abs(got - ref))) < 1e-15
+    bad = got.copy()
+    bad[7] = ref[7] + 1.01 * (2e-2 + 2e-2 * abs(ref[7]))
+    with pytest.raises(bench.ParityError):
+        bench.check_out(bad, ref, "bf16", "x")
+    with pytest.raises(bench.ParityError):
+        bench.check_out(np.where(np.arange(50) == 3, np.nan, got), ref, "bf16", "x")
+    with pytest.raises(bench.ParityError):
+        bench.check_out(got[:49], ref, "bf16", "x")
+    lse = np.array([300.0, -np.inf, 2.0])
+    assert bench.check_lse(lse + np.array([0.019, 0.0, -0.019]), lse, "bf16", "l") < 0.02
+    with pytest.raises(bench.ParityError):          # 0.03 on an LSE of 300 is out, however large the LSE
+        bench.check_lse(lse + np.array([0.03, 0.0, 0.0]), lse, "bf16", "l")
+    with pytest.raises(bench.ParityError):
+        bench.check_lse(np.array([300.0, 5.0, 2.0]), lse, "bf16", "l")

@@ -12,7 +12,7 @@ import torch
 import oracle as orc
 import paged_kv_cache_slots_amd as pkv
 import workloads as W
-from gpu_util import DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
+from gpu_util import assert_lse_close, DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
 from test_gpu_decode import split_only_bytes
 
 pytestmark = pytest.mark.gpu
@@ -66,7 +66,7 @@ def test_decode_step_parity(case, use_ws):
                                         q_dtype=c.q_dtype, k_scale=c.pool.k_scale, v_scale=c.pool.v_scale)
     tol = kv if kv != "f32" else "f32"
     assert_close(got, ref, tol, f"{name} out")
-    assert_close(got_lse, ref_lse, tol, f"{name} lse")
+    assert_lse_close(got_lse, ref_lse, tol, f"{name} lse")
     assert np.all(np.isfinite(got))
 
 

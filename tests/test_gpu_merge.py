@@ -9,7 +9,7 @@ import torch
 import oracle as orc
 import paged_kv_cache_slots_amd as pkv
 import workloads as W
-from gpu_util import DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
+from gpu_util import assert_lse_close, DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def test_merge_random_states(n_states, out_dtype):
     ref, ref_lse = orc.merge_states(o, lse)
     tol = "f32" if out_dtype == torch.float32 else "bf16"
     assert_close(as_f64(from_dev(out)), ref, tol, "merge out")
-    assert_close(from_dev(out_lse).astype(np.float64), ref_lse, "f32", "merge lse")
+    assert_lse_close(from_dev(out_lse).astype(np.float64), ref_lse, "f32", "merge lse")
     assert np.all(as_f64(from_dev(out))[3] == 0)
 
 
@@ -82,9 +82,8 @@ def test_shared_prefix_merge_equals_full_attention(size):
     got, got_lse, unshared = _shared_prefix_flow(c)
     kp = orc.scatter_slots(c.pool.k, c.new_k, c.slots)
     vp = orc.scatter_slots(c.pool.v, c.new_v, c.slots)
-    rows = range(c.q.shape[0]) if size == "small" else sorted({0, 17, 40, 77, 101, 127})
-    ref, ref_lse = orc.attn_decode(kp, vp, c.q, c.full_tables, c.full_lens, c.sm_scale, tables_subset=rows)
-    rows = list(rows)
+    rows = list(range(c.q.shape[0]))          # every row, at both sizes
+    ref, ref_lse = orc.attn_decode(kp, vp, c.q, c.full_tables, c.full_lens, c.sm_scale)
     assert_close(got[rows], ref[rows, 0], "bf16", "prefix+tail merged vs full attention")
-    assert_close(got_lse[rows], ref_lse[rows, 0], "bf16", "merged lse")
+    assert_lse_close(got_lse[rows], ref_lse[rows, 0], "bf16", "merged lse")
     assert_close(unshared[rows], ref[rows, 0], "bf16", "unshared decode")

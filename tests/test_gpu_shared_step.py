@@ -10,7 +10,7 @@ import torch
 import oracle as orc
 import paged_kv_cache_slots_amd as pkv
 import workloads as W
-from gpu_util import DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
+from gpu_util import assert_lse_close, DEV, as_f64, assert_close, from_dev, note, pool_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def check_shared(c, out_dtype=torch.bfloat16):
     tol = "fp8" if c.pool.dtype == "fp8" else "bf16"
     assert np.all(np.isfinite(got))
     assert_close(got, ref, tol, f"{c.name} out")
-    assert_close(got_lse, ref_lse, tol, f"{c.name} lse")
+    assert_lse_close(got_lse, ref_lse, tol, f"{c.name} lse")
 
 
 CASES = [

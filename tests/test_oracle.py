@@ -715,3 +715,90 @@ def test_shared_prefix_step_equals_step_over_joined_tables():
                                         0.25, kv_dtype="f32")
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- brute force on tiny inputs
+
+
+def _walk_keys(pool, table_row, length):
+    """Logical keys 0..length-1 of one row, found by walking the table page by
+    page and row by row in plain Python (no fancy indexing, no shifts)."""
+    page_size = pool.shape[1]
+    keys = []
+    page_index, offset = 0, 0
+    for _ in range(length):
+        keys.append(pool[int(table_row[page_index]), offset])
+        offset += 1
+        if offset == page_size:
+            page_index, offset = page_index + 1, 0
+    return keys
+
+
+def _brute_attention(q, keys, vals, scale):
+    """Softmax attention by its definition in plain Python floats: weights
+    exp(scale q.k_j) summed exactly with math.fsum, no max subtraction (the
+    tiny inputs keep every exponent small)."""
+    if not keys:
+        return [0.0] * len(q), -math.inf
+    w = [math.exp(scale * math.fsum(a * b for a, b in zip(q, k))) for k in keys]
+    total = math.fsum(w)
+    out = [math.fsum(wj * v[d] for wj, v in zip(w, vals)) / total for d in range(len(q))]
+    return out, math.log(total)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_and_prefill_equal_brute_force_on_tiny_inputs(seed):
+    """Tiny pools (D <= 8, lengths <= 40, pages of 4) through random tables:
+    the oracle's decode and block-causal prefill equal plain-Python attention
+    over keys found by walking the table slot by slot, to 1e-12."""
+    rng = np.random.default_rng(4000 + seed)
+    ps, hkv, group, d = 4, 2, 2, int(rng.choice([4, 8]))
+    hq = hkv * group
+    n_pages = 30
+    kp = rng.standard_normal((n_pages, ps, hkv, d)).astype(np.float32)
+    vp = rng.standard_normal((n_pages, ps, hkv, d)).astype(np.float32)
+    lens = [int(x) for x in rng.integers(0, 41, size=3)]
+    tables = np.stack([rng.permutation(n_pages)[:10] for _ in lens]).astype(np.int32)
+    q = rng.standard_normal((3, 1, hq, d)).astype(np.float32)
+    out, lse = orc.attn_decode(kp, vp, q, tables, lens, 0.4, kv_dtype="f32")
+    for t, L in enumerate(lens):
+        keys, vals = _walk_keys(kp, tables[t], L), _walk_keys(vp, tables[t], L)
+        for h in range(hq):
+            g = h // group
+            o, s = _brute_attention([float(x) for x in q[t, 0, h]], [[float(x) for x in k[g]] for k in keys],
+                                    [[float(x) for x in v[g]] for v in vals], 0.4)
+            np.testing.assert_allclose(out[t, 0, h], o, rtol=0, atol=1e-12)
+            assert (lse[t, 0, h] == s) if s == -math.inf else abs(lse[t, 0, h] - s) < 1e-12
+    # block-causal prefill: 9 queries in blocks of 4 over 13 cached keys (one padding row)
+    s_q, seq, n_ctx, cbs = 10, 9, 13, 4
+    qp = rng.standard_normal((1, s_q, hq, d)).astype(np.float32)
+    pout, plse = orc.attn_prefill_block_causal(kp, vp, qp, tables[:1], [n_ctx], [seq], cbs, 0.3, kv_dtype="f32")
+    for i in range(s_q):
+        count = n_ctx + min((i // cbs + 1) * cbs, seq) if i < seq else 0
+        keys, vals = _walk_keys(kp, tables[0], count), _walk_keys(vp, tables[0], count)
+        for h in range(hq):
+            g = h // group
+            o, s = _brute_attention([float(x) for x in qp[0, i, h]], [[float(x) for x in k[g]] for k in keys],
+                                    [[float(x) for x in v[g]] for v in vals], 0.3)
+            np.testing.assert_allclose(pout[0, i, h], o, rtol=0, atol=1e-12)
+            assert (plse[0, i, h] == s) if s == -math.inf else abs(plse[0, i, h] - s) < 1e-12
+
+
+def test_merge_over_every_subset_split_equals_whole():
+    """For a set of 10 keys, every one of the 2^10 ways to split it into a key
+    subset and its complement (either side possibly empty) merges back to the
+    attention over the whole set."""
+    rng = np.random.default_rng(77)
+    d, n = 6, 10
+    q = rng.standard_normal((2, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    whole, whole_lse = orc.attention_rows(q, k, v, 0.7)
+    for mask in range(1 << n):
+        a = [j for j in range(n) if mask >> j & 1]
+        b = [j for j in range(n) if not mask >> j & 1]
+        oa, la = orc.attention_rows(q, k[a], v[a], 0.7)
+        ob, lb = orc.attention_rows(q, k[b], v[b], 0.7)
+        o, lse = orc.merge_states(np.stack([oa, ob]), np.stack([la, lb]))
+        np.testing.assert_allclose(o, whole, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, whole_lse, rtol=0, atol=1e-12)

@@ -53,7 +53,9 @@ typedef enum {
   PKV_ERR_DTYPE = 3,       /* a dtype argument is not one of pkv_dtype           */
   PKV_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this combination          */
   PKV_ERR_HIP = 5,         /* a kernel launch failed (hipGetLastError)           */
-  PKV_ERR_ALIGN = 6        /* a pointer or stride breaks the stated alignment    */
+  PKV_ERR_ALIGN = 6,       /* a pointer or stride breaks the stated alignment    */
+  PKV_ERR_SCRATCH = 7      /* the call needs more scratch than the no-allocation
+                              entry point's device array holds                  */
 } pkv_status;
 
 typedef enum {
@@ -151,7 +153,11 @@ pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void
  *                pkv_attn_decode_workspace_bytes for the same shapes) used for
  *                cross-workgroup key splits and their merge.  With a NULL or
  *                smaller workspace the call runs unsplit (same result up to
- *                float rounding, possibly slower).
+ *                float rounding, possibly slower).  With a workspace, up to
+ *                8192 table rows run as one balanced persistent grid
+ *                (stream-K: the per-row tile prefix sums live in LDS); more
+ *                rows run as fixed key splits of >= 512 tokens (the pages'
+ *                rule), which balances less well on uneven lengths.
  * Kernels: q bf16 with K/V bf16 or fp8 run on bf16 MFMA; q fp32 (any K/V
  * dtype) runs on the vector ALUs.  head_dim 64 or 128.
  * sm_scale must be finite and > 0.
@@ -170,6 +176,30 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            int32_t max_kv_len, float sm_scale,
                            void* out, pkv_dtype out_dtype, float* out_lse,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_attn_decode_noalloc -- pkv_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Arguments, layouts, results and errors as pkv_attn_decode, without the
+ * workspace: the cross-workgroup state lives in a file-scope device array of
+ * 24 MiB that each GPU the library runs on holds until the process ends
+ * (its device address is looked up once per device).  The call allocates
+ * nothing.  The stream-K state of one workgroup per CU with head_dim 128 and
+ * up to 8192 table rows takes about 16.2 MiB on a 256-CU device; a call whose
+ * state does not fit (more than 8192 rows with key splits larger than the
+ * array, or a device of more than 340 CUs) returns PKV_ERR_SCRATCH and
+ * launches nothing.  Every call on one GPU uses that GPU's one array, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that can overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.
+ */
+pkv_status pkv_attn_decode_noalloc(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                   int32_t num_tables, int32_t rows_per_table, int32_t num_q_heads,
+                                   const int32_t* block_table, int32_t table_stride, const int32_t* kv_lens,
+                                   int32_t max_kv_len, float sm_scale,
+                                   void* out, pkv_dtype out_dtype, float* out_lse, hipStream_t stream);
 
 /*
  * pkv_attn_decode_step -- paged decode of a multi-token step (speculative

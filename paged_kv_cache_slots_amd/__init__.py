@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_DTYPE",
-                4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_HIP", 6: "PKV_ERR_ALIGN"}
+                4: "PKV_ERR_UNSUPPORTED", 5: "PKV_ERR_HIP", 6: "PKV_ERR_ALIGN", 7: "PKV_ERR_SCRATCH"}
 PKV_F32, PKV_BF16, PKV_FP8_E4M3FN = 0, 1, 2
 
 EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_attn_decode_workspace_bytes",
@@ -32,7 +32,7 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
-            "pkv_check_tables"]
+            "pkv_check_tables", "pkv_attn_decode_noalloc"]
 
 
 class PkvError(RuntimeError):
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_decode_step": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
                                                 ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_decode_noalloc": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
+                                                   ctypes.c_int, P, P]),
         "pkv_attn_decode_shared_prefix_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_decode_shared_prefix": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, I32, P, I32, P, I32, P,
                                                          I32, P, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
@@ -181,6 +183,22 @@ def pkv_attn_decode(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_l
         ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
         block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
         _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_decode_noalloc(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor,
+                            max_kv_len: int, sm_scale: float, out: torch.Tensor,
+                            out_lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Paged decode that allocates nothing: as ``pkv_attn_decode`` with the
+    cross-workgroup state in the library's per-device scratch array.  Calls
+    that can overlap on one GPU race on that array."""
+    if not q.is_contiguous() or not out.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q, out and block_table must be contiguous")
+    t, n, hq, _ = q.shape
+    ps = pool.struct()
+    _check("pkv_attn_decode_noalloc", load_library().pkv_attn_decode_noalloc(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
+        block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
+        _dtype_code(out.dtype), _ptr(out_lse), _stream(stream)))
 
 
 def pkv_attn_decode_step(pool: Pool, q: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor,

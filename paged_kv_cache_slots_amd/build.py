@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["pkv_api.hip", "scatter.hip", "merge.hip", "decode.hip", "prefill.hip", "commit.hip", "layout.hip", "check.hip"]
+SOURCES = ["pkv_api.hip", "scatter.hip", "merge.hip", "decode.hip", "prefill.hip", "commit.hip", "layout.hip", "check.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

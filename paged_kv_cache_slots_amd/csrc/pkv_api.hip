@@ -12,7 +12,7 @@ namespace {
 
 using namespace pkv;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 static_assert(kMaxCausalBlocks == PKV_MAX_CAUSAL_BLOCKS, "block limit of the ABI and the kernel differ");
 
 // Key splits of the decode: chunks of at least 512 tokens and at most 16
@@ -82,8 +82,8 @@ size_t decode_ws_bytes(int64_t rows, int32_t num_q_heads, int32_t head_dim, int 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 int64_t sk_cum_bytes(int32_t num_tables) { return align256(4 * (int64_t)(num_tables + 1)); }
 int64_t sk_rows() { return 2 * (int64_t)kMaxSkWaves * 16; }
-size_t sk_ws_bytes(int32_t num_tables, int32_t head_dim) {
-  return (size_t)(sk_cum_bytes(num_tables) + align256(sk_rows() * head_dim * 4) + align256(sk_rows() * 4));
+size_t sk_ws_bytes(int32_t num_tables, int32_t head_dim, int64_t rows = sk_rows()) {
+  return (size_t)(sk_cum_bytes(num_tables) + align256(rows * head_dim * 4) + align256(rows * 4));
 }
 
 // Compute units of the current device (queried once per device).
@@ -141,6 +141,7 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "no kernel for this head_dim / dtype / page_size combination";
     case PKV_ERR_HIP: return "kernel launch failed";
     case PKV_ERR_ALIGN: return "pointer or stride breaks the required alignment";
+    case PKV_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point's device array holds";
   }
   return "unknown status";
 }
@@ -198,11 +199,15 @@ size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_tabl
 
 // Decode of num_tables x rows_per_table query rows; with `causal` the rows of
 // a table row are the tokens of one step (row i sees len - (n - 1 - i) keys).
+// With `scratch` the workspace is the no-allocation entry point's device
+// array: the stream-K state is laid out for the launched grid only (2 slots x
+// 64 rows per workgroup), and a call whose state would not fit is refused
+// with PKV_ERR_SCRATCH instead of running with a smaller split.
 static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
                               int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
                               int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
                               void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
-                              size_t workspace_bytes, int32_t causal, hipStream_t stream) {
+                              size_t workspace_bytes, int32_t causal, hipStream_t stream, bool scratch = false) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
@@ -228,6 +233,14 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
     return PKV_ERR_ALIGN;
   }
 
+  if (scratch) {
+    // the device array of the no-allocation entry point (looked up once per
+    // device, after every argument check)
+    hipError_t e = hipSuccess;
+    workspace = noalloc_scratch(&e);
+    if (!workspace) return PKV_ERR_HIP;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   const int64_t rows = (int64_t)num_tables * rows_per_table;
   // Stream-K (balanced persistent grid) when the workspace holds its state.
   const int R = rows_per_table * (num_q_heads / pool->num_kv_heads);
@@ -235,10 +248,16 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   const int sk_rg = (int)ceil_div(ceil_div(R, 16), sk_wr);
   const int64_t sk_positions = (int64_t)num_tables * ceil_div(max_kv_len, 32) * pool->num_kv_heads * sk_rg;
   const int cus = use_mfma ? device_cu_count() : 0;
-  const bool use_sk = use_mfma && cus > 0 && workspace && aligned(workspace, 256) && num_tables <= kMaxSkTables &&
-                      workspace_bytes >= sk_ws_bytes(num_tables, D) && sk_positions < (int64_t(1) << 31);
+  // state rows of the stream-K slots: the public layout reserves them for the
+  // largest grid; the scratch layout for the grid this device launches
+  const int64_t sk_state_rows = scratch ? 128 * (int64_t)std::min(cus, kMaxSkWaves / 4) : sk_rows();
+  const bool sk_shape = use_mfma && cus > 0 && num_tables <= kMaxSkTables && sk_positions < (int64_t(1) << 31);
+  if (scratch && sk_shape && sk_ws_bytes(num_tables, D, sk_state_rows) > workspace_bytes) return PKV_ERR_SCRATCH;
+  const bool use_sk = sk_shape && workspace && aligned(workspace, 256) &&
+                      workspace_bytes >= sk_ws_bytes(num_tables, D, sk_state_rows);
   SplitPlan plan = plan_decode(max_kv_len);
   const size_t need = decode_ws_bytes(rows, num_q_heads, D, plan.splits);
+  if (scratch && !use_sk && plan.splits > 1 && need > workspace_bytes) return PKV_ERR_SCRATCH;
   if (use_sk || (plan.splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))) {
     plan.splits = 1;
     plan.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(max_kv_len, 32));
@@ -261,7 +280,7 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
     uint8_t* w = static_cast<uint8_t*>(workspace);
     p.ws_cum = reinterpret_cast<int32_t*>(w);
     p.ws_o = reinterpret_cast<float*>(w + sk_cum_bytes(num_tables));
-    p.ws_lse = reinterpret_cast<float*>(w + sk_cum_bytes(num_tables) + align256(sk_rows() * D * 4));
+    p.ws_lse = reinterpret_cast<float*>(w + sk_cum_bytes(num_tables) + align256(sk_state_rows * D * 4));
   } else if (plan.splits > 1) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + (int64_t)plan.splits * rows * num_q_heads * D;
@@ -315,6 +334,14 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            hipStream_t stream) {
   return decode_call(pool, q, q_dtype, num_tables, rows_per_table, num_q_heads, block_table, table_stride, kv_lens,
                      max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 0, stream);
+}
+
+pkv_status pkv_attn_decode_noalloc(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,
+                                   int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                                   void* out, pkv_dtype out_dtype, float* out_lse, hipStream_t stream) {
+  return decode_call(pool, q, q_dtype, num_tables, rows_per_table, num_q_heads, block_table, table_stride, kv_lens,
+                     max_kv_len, sm_scale, out, out_dtype, out_lse, nullptr, 0, 0, stream, true);
 }
 
 size_t pkv_attn_decode_shared_prefix_workspace_bytes(int32_t groups, int32_t samples, int32_t q_len,

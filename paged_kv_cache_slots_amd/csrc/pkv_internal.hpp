@@ -17,6 +17,15 @@ enum ElemType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 constexpr int kMaxSkTables = 8192;
 constexpr int kMaxSkWaves = 4096;
 
+// Device scratch of the no-allocation decode entry point (one array per GPU,
+// file scope in noalloc.hip): the stream-K state of a grid of one workgroup
+// per CU (2 slots x 64 rows per workgroup, 128 dims, LSE, and the prefix sums
+// of up to kMaxSkTables rows) fits for up to 340 CUs.
+constexpr size_t kNoAllocScratchBytes = size_t(24) << 20;
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress); NULL, with *err set, on failure.
+void* noalloc_scratch(hipError_t* err);
+
 // Prefill: workgroups of the persistent grid (2 partial-state slots each) and
 // the most leftover units an XCD splits along the keys.
 constexpr int kMaxPrefillWorkgroups = 512;

@@ -29,9 +29,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = pkv.load_library()
-    assert lib.pkv_abi_version() == 1
-    for code in range(7):
+    assert lib.pkv_abi_version() == 2
+    for code in range(8):
         assert lib.pkv_status_string(code)
+    assert b"scratch" in lib.pkv_status_string(7)
 
 
 def _pool(**kw):
@@ -258,3 +259,29 @@ def test_check_calls_argument_checks():
     assert lib.pkv_check_tables(ctypes.byref(p), None, 8, A, 4, A, None) == 1
     bad = _pool(page_size=48)
     assert lib.pkv_check_tables(ctypes.byref(bad), A, 8, A, 4, A, None) == 2
+
+
+def _decode_noalloc(pool, **kw):
+    a = dict(q=A, q_dtype=pkv.PKV_BF16, T=4, n=1, hq=32, table=A, tstride=128, lens=A, maxlen=4096, scale=0.1,
+             out=A, out_dtype=pkv.PKV_BF16, lse=None)
+    a.update(kw)
+    return pkv.load_library().pkv_attn_decode_noalloc(
+        ctypes.byref(pool), a["q"], a["q_dtype"], a["T"], a["n"], a["hq"], a["table"], a["tstride"], a["lens"],
+        a["maxlen"], a["scale"], a["out"], a["out_dtype"], a["lse"], None)
+
+
+@pytest.mark.parametrize("pool_kw,call_kw,expect", [
+    ({"k": None}, {}, 1),
+    ({}, {"q": None}, 1),
+    ({"dtype": pkv.PKV_FP8_E4M3FN}, {}, 1),                 # fp8 without scales
+    ({"page_size": 24}, {}, 2),
+    ({}, {"hq": 30}, 2),
+    ({}, {"maxlen": 128 * 32 + 1}, 2),
+    ({"head_dim": 96}, {}, 4),
+    ({}, {"q": A + 8}, 6),                                  # misaligned q
+    ({}, {"T": 0, "q": None, "out": None}, 0),              # empty: OK, nothing touched
+])
+def test_decode_noalloc_refuses_bad_arguments_on_the_host(pool_kw, call_kw, expect):
+    """The no-allocation decode checks its arguments like pkv_attn_decode, on
+    the host, before it looks up its device array or launches anything."""
+    assert _decode_noalloc(_pool(**pool_kw), **call_kw) == expect

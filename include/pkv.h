@@ -295,21 +295,29 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
  *   out_lse            NULL or float [batch, s_q, num_q_heads]; -inf for
  *                      padding rows.
  *   workspace          NULL, or device scratch of at least
- *                      pkv_attn_prefill_workspace_bytes(...) bytes (a fixed
- *                      65 MiB), 256-byte aligned, contents ignored.  With
- *                      it the query tiles left over after the last full
- *                      round of a persistent grid are split along the keys
- *                      and merged by a second kernel on the same stream; with
- *                      NULL (or too small / misaligned) they run whole.  Two
- *                      calls in flight at once need two workspaces.
+ *                      pkv_attn_prefill_workspace_bytes(...) bytes,
+ *                      256-byte aligned, contents ignored.  With it the query
+ *                      tiles left over after the last full round of a
+ *                      persistent grid are split along the keys and merged by
+ *                      a second kernel on the same stream; with NULL (or too
+ *                      small / misaligned) they run whole.  The size follows
+ *                      the shape and the current device's CU count: two
+ *                      partial states (66,560 bytes each) per workgroup of the
+ *                      grid when some XCD's share of the query tiles leaves a
+ *                      remainder to split, else 0 (no workspace needed).  On a
+ *                      machine without a device it assumes the largest grid
+ *                      (512 workgroups).  Two calls in flight at once need two
+ *                      workspaces.
  * Kernel: K/V bf16 (head_dim 128 or 64, page_size >= 16) on bf16 MFMA, or
  * fp8 e4m3fn with k_scale / v_scale (head_dim 128, page_size >= 32): the fp8
  * rows are moved to LDS as they are; QK^T runs on fp8 MFMA from the raw K
  * codes, with q held per row as two e4m3 code sets (about 2^-8 relative,
  * near bf16's own rounding), and PV on bf16 MFMA over V widened exactly in
  * LDS.  The fp8 MFMA accumulates less exactly than fp32 when one product
- * dominates a 64-dim block (a q row with a 4096x outlier: lse off by up to
- * 0.33), still inside the fp8 tolerance.  The scale of each (page, kv head) is applied in the softmax (K scale
+ * dominates a 64-dim block: a q row with one dim 4096x the others comes back
+ * with lse off by up to 0.33 (outputs within 0.05); rows whose largest
+ * entry is up to a few hundred times the rest stay within 0.06.  The scale
+ * of each (page, kv head) is applied in the softmax (K scale
  * on the scores, V scale on the probabilities and back out of their sum).  Scales
  * must be >= 0; a scale below 2^-100 acts as 2^-100 (so 0 gives keys of
  * score 0 and values of weight ~0, as code x 0 would, without 0 x inf).
@@ -327,6 +335,41 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
                                          int32_t causal_block_size, int32_t max_keys, float sm_scale,
                                          void* out, pkv_dtype out_dtype, float* out_lse,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_attn_prefill_block_causal_ragged -- the same prefill over a ragged
+ * batch: [P1] Description / Cache runs a forward's causal blocks as one
+ * ragged batch over the same table, each with its own key count, and block
+ * sizes come with the geometry (they need not be equal).
+ *
+ * As pkv_attn_prefill_block_causal, except for where rows live:
+ *   q_offsets          device int32 [batch + 1], non-decreasing: batch entry
+ *                      b owns rows q_offsets[b] .. q_offsets[b + 1] - 1 of q,
+ *                      out and out_lse (row i of entry b is row
+ *                      q_offsets[b] + i), and seq_len[b] <= that row count.
+ *                      Rows i in [seq_len[b], row count) are padding (0 and
+ *                      -inf); nothing past an entry's rows is read or
+ *                      written.
+ *   q                  row r, head h at q + r * q_tok_stride + h * q_head_stride.
+ *   out, out_lse       [q_offsets[batch], num_q_heads, head_dim] and
+ *                      [q_offsets[batch], num_q_heads].
+ *   max_rows           host upper bound of every entry's row count (it sizes
+ *                      the query tiles; the workspace size is
+ *                      pkv_attn_prefill_workspace_bytes with s_q = max_rows).
+ * The exact-window layout's per-block tables, n_ctx and seq_len (blocks of
+ * any sizes) drive it directly, with q_offsets the prefix sums of the block
+ * sizes.
+ * Errors: as pkv_attn_prefill_block_causal; NULL q_offsets -> PKV_ERR_NULL.
+ */
+pkv_status pkv_attn_prefill_block_causal_ragged(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                                int64_t q_tok_stride, int64_t q_head_stride,
+                                                int32_t batch, int32_t max_rows, int32_t num_q_heads,
+                                                const int32_t* q_offsets,
+                                                const int32_t* block_table, int32_t table_stride,
+                                                const int32_t* n_ctx, const int32_t* seq_len,
+                                                int32_t causal_block_size, int32_t max_keys, float sm_scale,
+                                                void* out, pkv_dtype out_dtype, float* out_lse,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pkv_merge_states -- join attention states over disjoint key sets.

@@ -32,7 +32,7 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
-            "pkv_check_tables", "pkv_attn_decode_noalloc"]
+            "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged"]
 
 
 class PkvError(RuntimeError):
@@ -85,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_prefill_block_causal": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, I32, P,
                                                          P, I32, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_prefill_block_causal_ragged": (ctypes.c_int, [PP, P, ctypes.c_int, I64, I64, I32, I32, I32, P, P,
+                                                                I32, P, P, I32, I32, F32, P, ctypes.c_int, P, P, SZ,
+                                                                P]),
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
         "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
         "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
@@ -271,6 +274,30 @@ def pkv_attn_prefill_block_causal(pool: Pool, q: torch.Tensor, block_table: torc
     _check("pkv_attn_prefill_block_causal", load_library().pkv_attn_prefill_block_causal(
         ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), q.stride(1), q.stride(2), b, s_q, hq,
         block_table.data_ptr(), block_table.stride(0), n_ctx.data_ptr(), seq_len.data_ptr(),
+        int(causal_block_size), int(max_keys), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype),
+        _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_prefill_block_causal_ragged(pool: Pool, q: torch.Tensor, q_offsets: torch.Tensor,
+                                         block_table: torch.Tensor, n_ctx: torch.Tensor, seq_len: torch.Tensor,
+                                         causal_block_size: int, max_rows: int, max_keys: int, sm_scale: float,
+                                         out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Block-causal prefill over a ragged batch.  ``q`` is a [T, Hq, D] view
+    (rows ``q_tok_stride`` apart, heads ``q_head_stride`` apart, D contiguous);
+    batch entry b owns rows ``q_offsets[b] .. q_offsets[b + 1] - 1`` (device
+    int32 [B + 1]); ``out`` is [T, Hq, D] contiguous, ``out_lse`` [T, Hq]."""
+    t, hq, d = q.shape
+    if q.stride(2) != 1:
+        raise ValueError("q must have D contiguous")
+    if not out.is_contiguous() or not block_table.is_contiguous() or q_offsets.dtype != torch.int32:
+        raise ValueError("out and block_table must be contiguous; q_offsets int32")
+    b = q_offsets.numel() - 1
+    ps = pool.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attn_prefill_block_causal_ragged", load_library().pkv_attn_prefill_block_causal_ragged(
+        ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), q.stride(0), q.stride(1), b, int(max_rows), hq,
+        q_offsets.data_ptr(), block_table.data_ptr(), block_table.stride(0), n_ctx.data_ptr(), seq_len.data_ptr(),
         int(causal_block_size), int(max_keys), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype),
         _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
 

@@ -462,18 +462,27 @@ pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q
 // ---------------------------------------------------------------------------
 size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_keys) {
-  (void)num_kv_heads; (void)head_dim; (void)max_keys;
-  if (batch <= 0 || s_q <= 0 || num_q_heads <= 0) return 0;
-  return (size_t)(2 * (int64_t)kMaxPrefillWorkgroups * (int64_t)prefill_slot_bytes());
+  (void)head_dim; (void)max_keys;
+  if (batch <= 0 || s_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  // Two partial-state slots per workgroup of the persistent grid, needed only
+  // when some XCD splits its leftover units along the keys.  Without a device
+  // to ask for its CU count, the largest grid is assumed.
+  const int cus = device_cu_count();
+  if (cus <= 0) return (size_t)(2 * (int64_t)kMaxPrefillWorkgroups * (int64_t)prefill_slot_bytes());
+  const int grid = prefill_grid(cus);
+  if (prefill_tail_units(batch, s_q, num_q_heads, num_kv_heads, grid) == 0) return 0;
+  return (size_t)(2 * (int64_t)grid * (int64_t)prefill_slot_bytes());
 }
 
-pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
-                                         int64_t q_tok_stride, int64_t q_head_stride, int32_t batch, int32_t s_q,
-                                         int32_t num_q_heads, const int32_t* block_table, int32_t table_stride,
-                                         const int32_t* n_ctx, const int32_t* seq_len, int32_t causal_block_size,
-                                         int32_t max_keys, float sm_scale, void* out, pkv_dtype out_dtype,
-                                         float* out_lse, void* workspace, size_t workspace_bytes,
-                                         hipStream_t stream) {
+// Block-causal prefill; with q_offsets (device int32 [batch + 1]) batch entry
+// b's rows are q_offsets[b] .. q_offsets[b + 1] - 1 of q / out / lse (ragged),
+// else b * s_q .. b * s_q + s_q - 1 (padded).
+static pkv_status prefill_call(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int64_t q_tok_stride,
+                               int64_t q_head_stride, int32_t batch, int32_t s_q, int32_t num_q_heads,
+                               const int32_t* q_offsets, const int32_t* block_table, int32_t table_stride,
+                               const int32_t* n_ctx, const int32_t* seq_len, int32_t causal_block_size,
+                               int32_t max_keys, float sm_scale, void* out, pkv_dtype out_dtype, float* out_lse,
+                               void* workspace, size_t workspace_bytes, bool ragged, hipStream_t stream) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
@@ -483,7 +492,7 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_keys > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;
   if (batch == 0 || s_q == 0) return PKV_OK;   // empty tensors may carry NULL pointers
-  if (!q || !block_table || !n_ctx || !seq_len || !out) return PKV_ERR_NULL;
+  if (!q || !block_table || !n_ctx || !seq_len || !out || (ragged && !q_offsets)) return PKV_ERR_NULL;
   const int D = pool->head_dim;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
@@ -492,7 +501,8 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   if (fp8 && (D != 128 || pool->page_size < 32)) return PKV_ERR_UNSUPPORTED;
   if (!aligned(pool->k, 16) || !aligned(pool->v, 16) || (pool->page_stride * elem_bytes(pool->dtype)) % 16 != 0 ||
       !aligned(q, 16) ||
-      (q_tok_stride * 2) % 16 != 0 || (q_head_stride * 2) % 16 != 0 || !aligned(out, 16))
+      (q_tok_stride * 2) % 16 != 0 || (q_head_stride * 2) % 16 != 0 || !aligned(out, 16) ||
+      (ragged && !aligned(q_offsets, 4)))
     return PKV_ERR_ALIGN;
 
   PrefillParams p;
@@ -505,6 +515,7 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   p.table = block_table;
   p.n_ctx = n_ctx;
   p.seq_len = seq_len;
+  p.q_offsets = ragged ? q_offsets : nullptr;
   p.out = out;
   p.out_lse = out_lse;
   p.page_stride = pool->page_stride;
@@ -527,6 +538,31 @@ pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pk
   if (need > 0 && cus > 0 && workspace && aligned(workspace, 256) && workspace_bytes >= need)
     p.ws_o = static_cast<float*>(workspace);
   return launch_prefill_mfma(p, D, cus, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_attn_prefill_block_causal(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                         int64_t q_tok_stride, int64_t q_head_stride, int32_t batch, int32_t s_q,
+                                         int32_t num_q_heads, const int32_t* block_table, int32_t table_stride,
+                                         const int32_t* n_ctx, const int32_t* seq_len, int32_t causal_block_size,
+                                         int32_t max_keys, float sm_scale, void* out, pkv_dtype out_dtype,
+                                         float* out_lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  return prefill_call(pool, q, q_dtype, q_tok_stride, q_head_stride, batch, s_q, num_q_heads, nullptr, block_table,
+                      table_stride, n_ctx, seq_len, causal_block_size, max_keys, sm_scale, out, out_dtype, out_lse,
+                      workspace, workspace_bytes, false, stream);
+}
+
+pkv_status pkv_attn_prefill_block_causal_ragged(const pkv_pool* pool, const void* q, pkv_dtype q_dtype,
+                                                int64_t q_tok_stride, int64_t q_head_stride, int32_t batch,
+                                                int32_t max_rows, int32_t num_q_heads, const int32_t* q_offsets,
+                                                const int32_t* block_table, int32_t table_stride,
+                                                const int32_t* n_ctx, const int32_t* seq_len,
+                                                int32_t causal_block_size, int32_t max_keys, float sm_scale,
+                                                void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream) {
+  return prefill_call(pool, q, q_dtype, q_tok_stride, q_head_stride, batch, max_rows, num_q_heads, q_offsets,
+                      block_table, table_stride, n_ctx, seq_len, causal_block_size, max_keys, sm_scale, out,
+                      out_dtype, out_lse, workspace, workspace_bytes, true, stream);
 }
 
 // ---------------------------------------------------------------------------

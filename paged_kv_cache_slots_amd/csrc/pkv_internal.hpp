@@ -107,6 +107,7 @@ struct PrefillParams {
   const int32_t* table;
   const int32_t* n_ctx;
   const int32_t* seq_len;
+  const int32_t* q_offsets;   // NULL: entry b's rows are b * s_q ..; else [batch + 1] row offsets
   void* out;
   float* out_lse;
   float* ws_o;                // stream-K partial states (NULL: leftover units run whole)
@@ -187,6 +188,8 @@ hipError_t launch_shared_prefix(const DecodeParams& pre, const DecodeParams& tai
                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
+int prefill_grid(int sm_count);
+int prefill_tail_units(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads, int grid);
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);
 hipError_t launch_copy_slots(const CopySlotsParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_causal_layout(const LayoutParams& p, hipStream_t stream);

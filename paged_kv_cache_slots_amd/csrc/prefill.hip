@@ -140,6 +140,16 @@ __device__ __forceinline__ void wait_dma_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Rows of batch entry b in q / out / lse: padded (b * s_q, s_q rows) or
+// ragged (q_offsets[b], q_offsets[b + 1] - q_offsets[b] rows).  Rows at or
+// past an entry's row count are neither read nor written.
+__device__ __forceinline__ int64_t entry_row0(const PrefillParams& p, int b) {
+  return p.q_offsets ? (int64_t)p.q_offsets[b] : (int64_t)b * p.s_q;
+}
+__device__ __forceinline__ int entry_rows(const PrefillParams& p, int b) {
+  return p.q_offsets ? p.q_offsets[b + 1] - p.q_offsets[b] : p.s_q;
+}
+
 __device__ __forceinline__ int visible_keys(int i, int n_ctx, int seq, int cbs) {
   if (i >= seq) return 0;
   const int e = (i / cbs + 1) * cbs;
@@ -160,7 +170,8 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* ptr) {
 
 // A unit: (batch, kv head, query head of the group, q-tile).
 struct Unit {
-  int b, g, h, row0, n_ctx, seq, cbs, kmax, tiles;
+  int b, g, h, row0, n_ctx, seq, cbs, kmax, tiles, rows;
+  int64_t qrow0;   // the entry's first row in q / out
 };
 
 __device__ __forceinline__ Unit unit_of(const PrefillParams& p, int u) {
@@ -175,6 +186,8 @@ __device__ __forceinline__ Unit unit_of(const PrefillParams& p, int u) {
   x.row0 = qt * kQT;
   x.n_ctx = p.n_ctx[x.b];
   x.seq = p.seq_len[x.b];
+  x.rows = entry_rows(p, x.b);
+  x.qrow0 = entry_row0(p, x.b);
   x.cbs = p.causal_block_size > 0 ? p.causal_block_size : (x.seq > 0 ? x.seq : 1);
   const int last = (x.row0 + kQT - 1 < x.seq - 1) ? x.row0 + kQT - 1 : x.seq - 1;
   x.kmax = x.row0 < x.seq ? visible_keys(last, x.n_ctx, x.seq, x.cbs) : 0;
@@ -228,10 +241,11 @@ __device__ __forceinline__ int64_t tail_chunk(int64_t tiles, int gx) {
 // Store this lane's part of a finished output row: the lane holds dims
 // 32 d + 8 (i / 4) + 4 hf + (i % 4) of row `row` of query head h.
 template <int D>
-__device__ __forceinline__ void store_rows(const PrefillParams& p, int b, int h, int row, int hf,
+__device__ __forceinline__ void store_rows(const PrefillParams& p, const Unit& x, int row, int hf,
                                            const f32x16 (&v)[D / 32], float lse) {
-  if (row >= p.s_q) return;
-  const int64_t orow = ((int64_t)b * p.s_q + row) * p.num_q_heads + h;
+  if (row >= x.rows) return;
+  const int h = x.h;
+  const int64_t orow = (x.qrow0 + row) * p.num_q_heads + h;
   if (p.out_bf16) {
     uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + orow * D;
 #pragma unroll
@@ -314,9 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     i32x8_t q8[2], q8l[2];
     float qsc = 1.f;
     {
-      const bool ok = my_row < x.seq;
-      const uint16_t* qp =
-          p.q + ((int64_t)x.b * p.s_q + (ok ? my_row : 0)) * p.q_tok_stride + (int64_t)x.h * p.q_head_stride;
+      const bool ok = my_row < x.seq && my_row < x.rows;
+      const uint16_t* qp = p.q + (x.qrow0 + (ok ? my_row : 0)) * p.q_tok_stride + (int64_t)x.h * p.q_head_stride;
       if constexpr (!kFp8) {
 #pragma unroll
         for (int s2 = 0; s2 < KSTEPS; ++s2) q[s2] = ok ? ld16(qp + 16 * s2 + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
     }
     const bool whole = t0 == 0 && t1 == ut;
     if (whole) {
-      if (kh == 0) store_rows<D>(p, x.b, x.h, my_row, hf, o, lse);
+      if (kh == 0) store_rows<D>(p, x, my_row, hf, o, lse);
     } else if (kh == 0) {
       // partial state -> slot (2 per workgroup: its chunk's first / last
       // segment); prefill_merge_kernel combines the pieces after this kernel
@@ -809,8 +822,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillPar
   // 32 g + 8 (i / 4) + 4 hf + (i % 4) (the MFMA accumulator layout)
   const Unit x = unit_of(p, plan.global_unit(plan.dp_units + k));
   const int row = x.row0 + 32 * rb + (lane & 31), hf = lane >> 5;
-  if (row >= p.s_q) return;
-  const int64_t orow = ((int64_t)x.b * p.s_q + row) * p.num_q_heads + x.h;
+  if (row >= x.rows) return;
+  const int64_t orow = (x.qrow0 + row) * p.num_q_heads + x.h;
   if (p.out_bf16) {
     uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + orow * D + 32 * g + 4 * hf;
 #pragma unroll
@@ -827,13 +840,34 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_merge_kernel(PrefillPar
     p.out_lse[orow] = m_all == kNegInf ? kNegInf : m_all + fast_log2(wsum) * kLn2;
 }
 
+// Persistent grid of the prefill: one workgroup per CU (8 waves, 2 per SIMD),
+// a multiple of 8 (one share per XCD).
+int prefill_grid(int sm_count) {
+  int g = sm_count > 0 ? sm_count : 8;
+  if (g > kMaxPrefillWorkgroups) g = kMaxPrefillWorkgroups;
+  return g < 8 ? 8 : (g / 8) * 8;
+}
+
+// The largest count of leftover units any XCD splits along the keys (the
+// kernels' xcd_plan with a workspace), 0 when every XCD's units divide
+// evenly over its workgroups.
+int prefill_tail_units(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads, int grid) {
+  const int64_t kv_units = (int64_t)batch * num_kv_heads;
+  const int64_t per_kv = (int64_t)(num_q_heads / num_kv_heads) * ((s_q + kQT - 1) / kQT);
+  const int gx = grid / 8;
+  int tail_units = 0;
+  for (int xcd = 0; xcd < 8; ++xcd) {
+    const int64_t nkv = kv_units > xcd ? (kv_units - xcd + 7) / 8 : 0;
+    const int64_t r = (nkv * per_kv) % gx;
+    if (r != 0 && r <= kMaxTailUnits && r > tail_units) tail_units = (int)r;
+  }
+  return tail_units;
+}
+
 hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_count, hipStream_t stream) {
   PrefillParams p = p0;
   p.q_tiles = (p.s_q + kQT - 1) / kQT;
-  // persistent grid: one workgroup per CU (8 waves, 2 per SIMD), a multiple of 8 (one share per XCD)
-  int g = sm_count > 0 ? sm_count : 8;
-  if (g > kMaxPrefillWorkgroups) g = kMaxPrefillWorkgroups;
-  g = g < 8 ? 8 : (g / 8) * 8;
+  const int g = prefill_grid(sm_count);
   if (p.kv_fp8)
     hipLaunchKernelGGL((prefill_kernel<128, true>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   else if (head_dim == 128)
@@ -842,17 +876,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
     hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.ws_o == nullptr) return e;
-  // merge only when some XCD splits its leftover units (the same test as the kernels')
-  const int64_t kv_units = (int64_t)p.batch * p.num_kv_heads;
-  const int64_t per_kv = (int64_t)p.group * p.q_tiles;
-  // (the grid covers the largest leftover count of any XCD)
-  const int gx = g / 8;
-  int tail_units = 0;
-  for (int xcd = 0; xcd < 8; ++xcd) {
-    const int64_t nkv = kv_units > xcd ? (kv_units - xcd + 7) / 8 : 0;
-    const int64_t r = (nkv * per_kv) % gx;
-    if (r != 0 && r <= kMaxTailUnits && r > tail_units) tail_units = (int)r;
-  }
+  // merge only when some XCD splits its leftover units (the same test as the
+  // kernels'); the grid covers the largest leftover count of any XCD
+  const int tail_units = prefill_tail_units(p.batch, p.s_q, p.num_q_heads, p.num_kv_heads, g);
   if (tail_units == 0) return e;
   const dim3 mgrid((unsigned)(4 * 8 * tail_units));
   if (head_dim == 128)

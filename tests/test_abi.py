@@ -285,3 +285,38 @@ def test_decode_noalloc_refuses_bad_arguments_on_the_host(pool_kw, call_kw, expe
     """The no-allocation decode checks its arguments like pkv_attn_decode, on
     the host, before it looks up its device array or launches anything."""
     assert _decode_noalloc(_pool(**pool_kw), **call_kw) == expect
+
+
+def _prefill_ragged(pool, **kw):
+    a = dict(q=A, q_dtype=pkv.PKV_BF16, qts=8 * 128, qhs=128, B=3, max_rows=200, hq=8, offs=A, table=A, tstride=64,
+             n_ctx=A, seq=A, cbs=0, max_keys=1000, scale=0.1, out=A, out_dtype=pkv.PKV_BF16, lse=None, ws=None,
+             wsb=0)
+    a.update(kw)
+    return pkv.load_library().pkv_attn_prefill_block_causal_ragged(
+        ctypes.byref(pool), a["q"], a["q_dtype"], a["qts"], a["qhs"], a["B"], a["max_rows"], a["hq"], a["offs"],
+        a["table"], a["tstride"], a["n_ctx"], a["seq"], a["cbs"], a["max_keys"], a["scale"], a["out"],
+        a["out_dtype"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("pool_kw,call_kw,expect", [
+    ({}, {"offs": None}, 1),                                # the row offsets are required
+    ({}, {"q": None}, 1),
+    ({}, {"hq": 7}, 2),                                     # Hq % Hkv != 0
+    ({}, {"max_keys": 64 * 32 + 1}, 2),                     # beyond the table's capacity
+    ({"head_dim": 96}, {}, 4),
+    ({}, {"offs": A + 2}, 6),                               # misaligned int32 offsets
+    ({}, {"B": 0, "q": None, "offs": None}, 0),             # empty batch: OK, nothing touched
+])
+def test_prefill_ragged_refuses_bad_arguments_on_the_host(pool_kw, call_kw, expect):
+    assert _prefill_ragged(_pool(**pool_kw), **call_kw) == expect
+
+
+def test_prefill_workspace_size_without_a_device_is_the_largest_grid():
+    """With no device to ask for its CU count the size covers the largest grid
+    (512 workgroups x 2 partial states); a shape with no batch needs none."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: the size follows its CU count (checked by the GPU prefill tests)")
+    lib = pkv.load_library()
+    assert lib.pkv_attn_prefill_workspace_bytes(1, 1568, 24, 24, 128, 6680) == 2 * 512 * 66560
+    assert lib.pkv_attn_prefill_workspace_bytes(0, 1568, 24, 24, 128, 6680) == 0

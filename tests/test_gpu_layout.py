@@ -142,11 +142,23 @@ class Rollout:
         pkv.pkv_causal_layout(self.lay, self.table, self.priv, self.committed, self.evicted)
         pkv.pkv_copy_slots(self.pool, self.lay.commit_src, self.lay.commit_dst)
 
-    def forward(self, k_new, v_new, q, out=None):
-        """k_new / v_new [T, Hkv, D] and q [T, Hq, D] bf16 on the device."""
+    def forward(self, k_new, v_new, q, out=None, ragged=False):
+        """k_new / v_new [T, Hkv, D] and q [T, Hq, D] bf16 on the device.
+        Equal blocks run the padded prefill ([nb, cbs, Hq, D] output); with
+        ``ragged`` (any block sizes) the ragged one ([T, Hq, D] output, block b
+        at rows offsets[b] ..)."""
         lay = self.lay
         pkv.pkv_scatter_slots(self.pool, k_new, v_new, lay.stage_slots, slots2=lay.stage_slots2)
         pkv.pkv_copy_slots(self.pool, lay.current_src, lay.current_dst)
+        if ragged:
+            total = sum(self.sizes)
+            offs = torch.tensor(np.concatenate([[0], np.cumsum(self.sizes)]).astype(np.int32), device=DEV)
+            if out is None:
+                out = torch.empty((total, self.hq, self.d), dtype=torch.float32, device=DEV)
+            max_keys = self.pin + self.window + max(self.sizes)
+            pkv.pkv_attn_prefill_block_causal_ragged(self.pool, q, offs, lay.block_tables, lay.n_ctx, lay.seq_len, 0,
+                                                     max(self.sizes), max_keys, 1.0 / math.sqrt(self.d), out)
+            return out
         nb, cbs = len(self.sizes), self.sizes[0]
         if out is None:
             out = torch.empty((nb, cbs, self.hq, self.d), dtype=torch.float32, device=DEV)
@@ -177,7 +189,7 @@ def _dense_reference(keys_all, vals_all, q, start, sizes, pin, window, hq, hkv):
                                             vals_all[vis, h // group], 1.0 / math.sqrt(q.shape[-1]))
         out.append(o)
         s += size
-    return np.stack(out)
+    return np.stack(out) if len(set(sizes)) == 1 else np.concatenate(out)
 
 
 @pytest.mark.parametrize("geom", [
@@ -205,6 +217,38 @@ def test_exact_window_rollout_attention(geom):
         torch.cuda.synchronize()
         ref = _dense_reference(as_f64(keys), as_f64(vals), as_f64(q), c, sizes, pin, window, hq, hkv)
         assert_close(from_dev(out), ref, "bf16", f"step {step}")
+        if n:
+            ro.commit(n)
+
+
+@pytest.mark.parametrize("geom", [
+    # ps, pin, window, block sizes, commits, Hq, Hkv, D
+    (32, 40, 100, [24, 17, 40], [81, 81, 81, 81], 4, 2, 128),
+    (16, 16, 64, [5, 33], [38, 38, 38, 38, 20], 8, 2, 64),
+    (32, 0, 300, [1, 64, 31, 64], [160, 160, 160], 2, 1, 128),
+    (16, 37, 0, [20, 3, 9], [32, 32, 32], 4, 4, 128),
+    (32, 40, 100, [24, 24, 24], [72, 72, 72], 4, 2, 128),
+], ids=lambda g: f"ps{g[0]}_pin{g[1]}_w{g[2]}_blocks{'-'.join(map(str, g[3]))}")
+def test_exact_window_rollout_with_unequal_causal_blocks(geom):
+    """Causal blocks of different sizes in one forward, run as one ragged
+    batch over the layout's per-block tables (no padding copy), against
+    float64 attention of each block over its visible keys, across commits."""
+    ps, pin, window, sizes, commits, hq, hkv, d = geom
+    total = sum(sizes)
+    rng = np.random.default_rng(ps + pin + window + total)
+    n_keys = sum(commits) + total
+    keys = to_storage(rng.standard_normal((n_keys, hkv, d)).astype(np.float32), "bf16")
+    vals = to_storage(rng.standard_normal((n_keys, hkv, d)).astype(np.float32), "bf16")
+    ro = Rollout(13, ps, pin, window, sizes, hq, hkv, d)
+    ro.commit_layout()
+    for step, n in enumerate(commits + [0]):
+        c = ro.committed
+        q = to_storage(rng.standard_normal((total, hq, d)).astype(np.float32), "bf16")
+        note(f"exact window ragged geom={geom} step={step} committed={c} evicted={ro.evicted}")
+        out = ro.forward(to_dev(keys[c:c + total]), to_dev(vals[c:c + total]), to_dev(q), ragged=True)
+        torch.cuda.synchronize()
+        ref = _dense_reference(as_f64(keys), as_f64(vals), as_f64(q), c, sizes, pin, window, hq, hkv)
+        assert_close(from_dev(out), ref.reshape(total, hq, d), "bf16", f"step {step}")
         if n:
             ro.commit(n)
 

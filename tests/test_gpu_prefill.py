@@ -294,3 +294,63 @@ def test_prefill_fp8_full_size(use_ws):
     queries in 1568 rows, one causal block) over an fp8 pool: every row."""
     c = W.make_fp8_prefill_case("fp8_full", 98, 1098, 1, 1568, [1560], [5120], 24, 24, 128, 32, 1560)
     check_fp8(c, use_ws=use_ws)
+
+
+# --------------------------------------------------------------------------- ragged batches
+
+def _ragged_case(seed):
+    """A padded block-causal case whose entries get their own row counts
+    (seq_len up to seq_len + 3 padding rows, capped at s_q) for the ragged
+    layout; rows are packed entry after entry."""
+    rng = np.random.default_rng(1500 + seed)
+    b = int(rng.integers(1, 5))
+    s_q = int(rng.integers(20, 260))
+    seqs = [int(x) for x in rng.integers(0, s_q + 1, size=b)]
+    seqs[0] = max(seqs[0], 1)
+    ctxs = [int(x) for x in rng.integers(0, 700, size=b)]
+    hkv = int(rng.choice([1, 2, 3]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    ps = int(rng.choice([16, 32, 64]))
+    cbs = int(rng.choice([0, 1, 13, 64]))
+    c = W.make_prefill_case(f"ragged{seed}", 1600 + seed, 2600 + seed, b, s_q, seqs, ctxs, hq, hkv, d, ps, cbs,
+                            num_pool_pages=sum(math.ceil((x + y) / ps) for x, y in zip(seqs, ctxs)) + 5,
+                            extra_table_cols=2)
+    rows = [min(s_q, sq + int(rng.integers(0, 4))) for sq in seqs]
+    return c, rows
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_ragged_rows_match_the_padded_oracle(seed):
+    """The ragged entry point on rows packed entry after entry (each entry its
+    own row count, some with padding rows, some empty) equals the oracle of
+    the padded layout row for row; rows past the last entry are untouched."""
+    c, rows = _ragged_case(seed)
+    b, s_q, hq, d = c.qkv.shape[0], c.s_q, c.num_q_heads, c.qkv.shape[-1]
+    hkv = c.num_kv_heads
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    total = int(offs[-1])
+    pool = pool_to_dev(c.pool)
+    qkv = to_dev(c.qkv)
+    flat = qkv.view(b * s_q, hq + 2 * hkv, d)
+    pkv.pkv_scatter_slots(pool, flat[:, hq:hq + hkv], flat[:, hq + hkv:], to_dev(c.slots))
+    q_r = torch.cat([qkv[bb, :rows[bb], :hq] for bb in range(b)]) if total else torch.empty(
+        (0, hq, d), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((total + 5, hq, d), 7.0, dtype=torch.float32, device=DEV)
+    lse = torch.full((total + 5, hq), 7.0, dtype=torch.float32, device=DEV)
+    max_rows = max(rows)
+    nb = pkv.pkv_attn_prefill_workspace_bytes(b, max_rows, hq, hkv, d, c.max_keys)
+    ws = torch.full((max(nb, 16),), 0xFF, dtype=torch.uint8, device=DEV) if seed % 2 == 0 else None
+    note(f"prefill ragged {c.name} B={b} rows={rows} seq={list(c.seq_len)} n_ctx={list(c.n_ctx)} Hq={hq} "
+         f"Hkv={hkv} D={d} ps={c.pool.page_size} cbs={c.causal_block_size} ws={ws is not None}")
+    pkv.pkv_attn_prefill_block_causal_ragged(pool, q_r, to_dev(offs), to_dev(c.tables), to_dev(c.n_ctx),
+                                             to_dev(c.seq_len), c.causal_block_size, max_rows, c.max_keys,
+                                             c.sm_scale, out[:total], lse[:total], ws)
+    torch.cuda.synchronize()
+    got, got_lse = from_dev(out).astype(np.float64), from_dev(lse).astype(np.float64)
+    ref, ref_lse = oracle_prefill(c)
+    want = np.concatenate([ref[bb, :rows[bb]] for bb in range(b)])
+    want_lse = np.concatenate([ref_lse[bb, :rows[bb]] for bb in range(b)])
+    assert_close(got[:total], want, "bf16", f"{c.name} out")
+    assert_lse_close(got_lse[:total], want_lse, "bf16", f"{c.name} lse")
+    assert np.all(got[total:] == 7.0) and np.all(got_lse[total:] == 7.0), "rows past the last entry were written"

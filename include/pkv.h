@@ -43,8 +43,10 @@
 extern "C" {
 #endif
 
-/* Same type as HIP's own hipStream_t (a repeated identical typedef is legal). */
+/* Same types as HIP's own hipStream_t and hipEvent_t (a repeated identical
+ * typedef is legal). */
 typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
 
 typedef enum {
   PKV_OK = 0,
@@ -176,6 +178,17 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            int32_t max_kv_len, float sm_scale,
                            void* out, pkv_dtype out_dtype, float* out_lse,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_set_timing_event -- measurement hook.  While ev is not NULL, every
+ * pkv_attn_decode / pkv_attn_decode_noalloc / pkv_attn_decode_step and
+ * prefill call records ev on its stream right after its main kernel, before
+ * a merge kernel of split work, so that a caller can time the dominant kernel
+ * of a call alone with HIP events (the whole call is timed with events around
+ * it).  NULL turns it off.  Process-wide and not synchronised: set it while
+ * no other host thread calls the library.  The event is the caller's.
+ */
+void pkv_set_timing_event(hipEvent_t ev);
 
 /*
  * pkv_attn_decode_noalloc -- pkv_attn_decode for callers that cannot

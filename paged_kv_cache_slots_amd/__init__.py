@@ -32,7 +32,8 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_merge_states", "pkv_rotate_rows", "pkv_copy_slots", "pkv_causal_layout_bounds",
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
-            "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged"]
+            "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged",
+            "pkv_set_timing_event"]
 
 
 class PkvError(RuntimeError):
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                 I32, P, P, I32, I32, F32, P, ctypes.c_int, P, P, SZ,
                                                                 P]),
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
+        "pkv_set_timing_event": (None, [P]),
         "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
         "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
         "pkv_causal_layout_bounds": (ctypes.c_int, [I32, I64, I64, P, I32, ctypes.POINTER(PkvCausalBounds)]),
@@ -300,6 +302,12 @@ def pkv_attn_prefill_block_causal_ragged(pool: Pool, q: torch.Tensor, q_offsets:
         q_offsets.data_ptr(), block_table.data_ptr(), block_table.stride(0), n_ctx.data_ptr(), seq_len.data_ptr(),
         int(causal_block_size), int(max_keys), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype),
         _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_set_timing_event(event: Optional["torch.cuda.Event"]) -> None:
+    """While set, the library records ``event`` on a call's stream right after
+    its main kernel (before a merge kernel); None turns it off."""
+    load_library().pkv_set_timing_event(None if event is None else event.cuda_event)
 
 
 def pkv_merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor,

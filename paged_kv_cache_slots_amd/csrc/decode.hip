@@ -1075,6 +1075,7 @@ static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  record_timing_event(stream);
   const int R = p.rows_per_table * p.group;
   const int64_t total = (int64_t)p.num_tables * p.num_kv_heads * R * (D / 4);
   hipLaunchKernelGGL(merge_sk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p, WR, D);

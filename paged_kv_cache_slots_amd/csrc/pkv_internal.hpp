@@ -176,6 +176,10 @@ struct LayoutParams {
   int64_t* current_dst;
 };
 
+// Measurement hook: records the event set by pkv_set_timing_event (if any)
+// on `stream`, right after a call's main kernel and before its merge kernel.
+void record_timing_event(hipStream_t stream);
+
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);

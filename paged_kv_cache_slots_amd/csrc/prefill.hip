@@ -875,7 +875,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
   else
     hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.ws_o == nullptr) return e;
+  if (e != hipSuccess) return e;
+  record_timing_event(stream);
+  if (p.ws_o == nullptr) return e;
   // merge only when some XCD splits its leftover units (the same test as the
   // kernels'); the grid covers the largest leftover count of any XCD
   const int tail_units = prefill_tail_units(p.batch, p.s_q, p.num_q_heads, p.num_kv_heads, g);

@@ -202,20 +202,23 @@ class Flusher:
 
 
 def time_kernel_events(torch, pkv, step, reps, flush=None):
-    """Median (ms) from an event before ``step`` to the event the library
-    records right after the call's main kernel (before any merge kernel)."""
+    """Median (ms) of a call's main kernel alone: the library launches it with
+    a start / stop event pair (hipExtLaunchKernel), which take the kernel's own
+    start and end times."""
     times = []
     for _ in range(reps):
         if flush:
             flush()
-        a, m = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        m.record()
-        a.record()
-        pkv.pkv_set_timing_event(m)
-        step()
-        pkv.pkv_set_timing_event(None)
+        ks, ke = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ks.record()     # creates the events; the launch sets them again
+        ke.record()
+        pkv.pkv_set_timing_events(ks, ke)
+        try:
+            step()
+        finally:
+            pkv.pkv_set_timing_events(None, None)
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(m))
+        times.append(ks.elapsed_time(ke))
     return float(np.median(times))
 
 
@@ -266,23 +269,24 @@ def run_headline(args, torch, pkv, W):
     def step(record=False, kernel=False):
         pkv.pkv_scatter_slots(dev["pool"], dev["new_k"], dev["new_v"], dev["slots"])
         if record:
-            # a: before the call; b: after it.  With `kernel`, m is recorded by
-            # the library right after the decode kernel (before the merge
-            # kernel of the split units); that extra record lengthens the call,
-            # so calls and kernels are timed in steps of their own.
-            a, m, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            # a: before the call; b: after it.  With `kernel`, the library
+            # launches the decode kernel with the pair (ks, ke), which take
+            # that kernel's own start and end (not the merge kernel of the
+            # split units); calls and kernels are timed in steps of their own.
+            a, ks, ke, b = (torch.cuda.Event(enable_timing=True) for _ in range(4))
             if kernel:
-                m.record()      # creates the event; the library records it again
+                ks.record()     # creates the events; the launch sets them again
+                ke.record()
             a.record()
             if kernel:
-                pkv.pkv_set_timing_event(m)
+                pkv.pkv_set_timing_events(ks, ke)
         pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], case.max_kv_len, case.sm_scale,
                             dev["out"], None, dev["ws"])
         if record:
             if kernel:
-                pkv.pkv_set_timing_event(None)
+                pkv.pkv_set_timing_events(None, None)
             b.record()
-            ev.append((a, m if kernel else None, b))
+            ev.append((a, (ks, ke) if kernel else None, b))
 
     # parity gate: the first step's output against the oracle (whole batch)
     import oracle as orc
@@ -319,7 +323,7 @@ def run_headline(args, torch, pkv, W):
     for _ in range(args.steps):
         step(record=True, kernel=True)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(m) for a, m, _ in ev]))
+    kern_ms = float(np.mean([ks.elapsed_time(ke) for _, (ks, ke), _ in ev]))
     # the scatter's own latency, in steps of its own (outside the timed loop:
     # an extra event inside it would lengthen every step)
     sev = []
@@ -866,10 +870,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "kernel": "decode_skh_kernel (the dominant kernel of the pkv_attn_decode call)",
                      "timing": "HIP events on the launch stream over --steps further steps (not inside the "
-                               "wall-clock loop, where they lengthen every step): one before the call and one the "
-                               "library records right after the decode kernel, before the merge kernel of the "
-                               "split units; the span includes the kernel's dispatch latency, which a profiler's "
-                               "kernel duration does not",
+                               "wall-clock loop): the library launches the decode kernel through "
+                               "hipExtLaunchKernel with a start / stop event pair, which take that kernel's own "
+                               "start and end times (the merge kernel of the split units is outside the span)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_kernel_ms"], 5),
                      "call": {"what": "the whole pkv_attn_decode call: decode kernel + merge kernel of the split "
                                       "units + the gap between them",

@@ -180,15 +180,19 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * pkv_set_timing_event -- measurement hook.  While ev is not NULL, every
- * pkv_attn_decode / pkv_attn_decode_noalloc / pkv_attn_decode_step and
- * prefill call records ev on its stream right after its main kernel, before
- * a merge kernel of split work, so that a caller can time the dominant kernel
- * of a call alone with HIP events (the whole call is timed with events around
- * it).  NULL turns it off.  Process-wide and not synchronised: set it while
- * no other host thread calls the library.  The event is the caller's.
+ * pkv_set_timing_events -- measurement hook.  While start or stop is not
+ * NULL, the main kernel of every pkv_attn_decode / pkv_attn_decode_noalloc /
+ * pkv_attn_decode_step / prefill call (the stream-K, split or fp32 decode
+ * kernel; the prefill kernel; not a merge kernel of split work) is launched
+ * through hipExtLaunchKernel with these events, which then carry that
+ * kernel's own start and end times: hipEventElapsedTime(start, stop) is the
+ * kernel's duration, with no marker between it and its neighbours.  Each
+ * such launch sets both events again, so after a call they hold its main
+ * kernel's times.  NULL, NULL turns the hook off.  Process-wide and not
+ * synchronised: set it while no other host thread calls the library.  The
+ * events are the caller's, created before the call.
  */
-void pkv_set_timing_event(hipEvent_t ev);
+void pkv_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 /*
  * pkv_attn_decode_noalloc -- pkv_attn_decode for callers that cannot

@@ -33,7 +33,7 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
             "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged",
-            "pkv_set_timing_event"]
+            "pkv_set_timing_events"]
 
 
 class PkvError(RuntimeError):
@@ -90,7 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                 I32, P, P, I32, I32, F32, P, ctypes.c_int, P, P, SZ,
                                                                 P]),
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
-        "pkv_set_timing_event": (None, [P]),
+        "pkv_set_timing_events": (None, [P, P]),
         "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
         "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
         "pkv_causal_layout_bounds": (ctypes.c_int, [I32, I64, I64, P, I32, ctypes.POINTER(PkvCausalBounds)]),
@@ -304,10 +304,13 @@ def pkv_attn_prefill_block_causal_ragged(pool: Pool, q: torch.Tensor, q_offsets:
         _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def pkv_set_timing_event(event: Optional["torch.cuda.Event"]) -> None:
-    """While set, the library records ``event`` on a call's stream right after
-    its main kernel (before a merge kernel); None turns it off."""
-    load_library().pkv_set_timing_event(None if event is None else event.cuda_event)
+def pkv_set_timing_events(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
+    """While set, a call's main kernel (not its merge kernel) is launched with
+    ``start`` / ``stop``, which then hold that kernel's own start and end
+    times; None, None turns it off.  The events must have been created (e.g.
+    recorded once) before the call."""
+    lib = load_library()
+    lib.pkv_set_timing_events(None if start is None else start.cuda_event, None if stop is None else stop.cuda_event)
 
 
 def pkv_merge_states(o_parts: torch.Tensor, lse_parts: torch.Tensor, out: torch.Tensor,

@@ -1032,14 +1032,14 @@ static hipError_t launch_mfma_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 block(256);
   if (blocks16 <= 1) {
     const dim3 grid(p.num_tables, p.num_kv_heads, p.splits);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 4>), grid, block, 0, stream, p);
+    PKV_LAUNCH_MAIN((decode_mfma_kernel<D, kFp8, 4>), grid, block, 0, stream, p);
   } else if (blocks16 <= 2) {
     const dim3 grid(p.num_tables, p.num_kv_heads, p.splits);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 2>), grid, block, 0, stream, p);
+    PKV_LAUNCH_MAIN((decode_mfma_kernel<D, kFp8, 2>), grid, block, 0, stream, p);
   } else {
     const int rg = (blocks16 + 3) / 4;
     const dim3 grid(p.num_tables * rg, p.num_kv_heads, p.splits);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, kFp8, 1>), grid, block, 0, stream, p);
+    PKV_LAUNCH_MAIN((decode_mfma_kernel<D, kFp8, 1>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -1068,14 +1068,13 @@ static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream)
   const int grid = sm_count < kMaxSkWaves / 4 ? sm_count : kMaxSkWaves / 4;
   if (p.head_par) {
     p.n_workers = grid;
-    hipLaunchKernelGGL((decode_skh_kernel<D, kFp8>), dim3(grid), dim3(256), 0, stream, p);
+    PKV_LAUNCH_MAIN((decode_skh_kernel<D, kFp8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
     p.n_workers = grid * (4 / WR);
-    hipLaunchKernelGGL((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
+    PKV_LAUNCH_MAIN((decode_sk_kernel<D, kFp8, WR>), dim3(grid), dim3(256), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  record_timing_event(stream);
   const int R = p.rows_per_table * p.group;
   const int64_t total = (int64_t)p.num_tables * p.num_kv_heads * R * (D / 4);
   hipLaunchKernelGGL(merge_sk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p, WR, D);
@@ -1132,9 +1131,9 @@ hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, in
 template <int D, int QT>
 static hipError_t launch_valu_dq(const DecodeParams& p, ElemType kv, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.num_tables * p.rows_per_table * p.num_q_heads), p.splits), block(64);
-  if (kv == kF32) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kF32>), grid, block, 0, stream, p);
-  else if (kv == kBF16) hipLaunchKernelGGL((decode_valu_kernel<D, QT, kBF16>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((decode_valu_kernel<D, QT, kFP8>), grid, block, 0, stream, p);
+  if (kv == kF32) PKV_LAUNCH_MAIN((decode_valu_kernel<D, QT, kF32>), grid, block, 0, stream, p);
+  else if (kv == kBF16) PKV_LAUNCH_MAIN((decode_valu_kernel<D, QT, kBF16>), grid, block, 0, stream, p);
+  else PKV_LAUNCH_MAIN((decode_valu_kernel<D, QT, kFP8>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -131,16 +131,14 @@ int64_t evicted_tokens(int64_t ps, int64_t pin, int64_t window, int64_t committe
 }  // namespace
 
 namespace pkv {
-// The event of pkv_set_timing_event (process-wide; NULL: off).
-static hipEvent_t g_timing_event = nullptr;
-void record_timing_event(hipStream_t stream) {
-  if (g_timing_event) (void)hipEventRecord(g_timing_event, stream);
-}
+// The events of pkv_set_timing_events (process-wide; NULL: off).
+static TimingEvents g_timing = {nullptr, nullptr};
+TimingEvents timing_events() { return g_timing; }
 }  // namespace pkv
 
 extern "C" {
 
-void pkv_set_timing_event(hipEvent_t ev) { pkv::g_timing_event = ev; }
+void pkv_set_timing_events(hipEvent_t start, hipEvent_t stop) { pkv::g_timing = {start, stop}; }
 
 const char* pkv_status_string(pkv_status s) {
   switch (s) {
@@ -317,7 +315,6 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   hipError_t e = use_mfma ? launch_decode_mfma(p, elem_type(pool->dtype), D, stream)
                           : launch_decode_valu(p, elem_type(q_dtype), elem_type(pool->dtype), D, stream);
   if (e != hipSuccess) return PKV_ERR_HIP;
-  record_timing_event(stream);
   if (plan.splits > 1) {
     MergeParams m;
     m.o_parts = p.ws_o;

@@ -3,6 +3,7 @@
 // kernels take by value.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -176,9 +177,29 @@ struct LayoutParams {
   int64_t* current_dst;
 };
 
-// Measurement hook: records the event set by pkv_set_timing_event (if any)
-// on `stream`, right after a call's main kernel and before its merge kernel.
-void record_timing_event(hipStream_t stream);
+// Measurement hook (pkv_set_timing_events): the events a call's main kernel
+// is launched with; both NULL when the hook is off.
+struct TimingEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+TimingEvents timing_events();
+
+}  // namespace pkv
+
+// Launch of a call's main kernel.  With the hook on it goes through
+// hipExtLaunchKernel, whose events take the kernel dispatch's own start and
+// end times; otherwise it is a plain launch.
+#define PKV_LAUNCH_MAIN(kernel, grid, block, smem, stream, ...)                                            \
+  do {                                                                                                     \
+    const ::pkv::TimingEvents ev_ = ::pkv::timing_events();                                                \
+    if (ev_.start || ev_.stop)                                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, smem, stream, ev_.start, ev_.stop, 0u, __VA_ARGS__);      \
+    else                                                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, smem, stream, __VA_ARGS__);                                  \
+  } while (0)
+
+namespace pkv {
 
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);

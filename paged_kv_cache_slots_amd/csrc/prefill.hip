@@ -869,14 +869,13 @@ hipError_t launch_prefill_mfma(const PrefillParams& p0, int head_dim, int sm_cou
   p.q_tiles = (p.s_q + kQT - 1) / kQT;
   const int g = prefill_grid(sm_count);
   if (p.kv_fp8)
-    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+    PKV_LAUNCH_MAIN((prefill_kernel<128, true>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+    PKV_LAUNCH_MAIN((prefill_kernel<128, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
+    PKV_LAUNCH_MAIN((prefill_kernel<64, false>), dim3((unsigned)g), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  record_timing_event(stream);
   if (p.ws_o == nullptr) return e;
   // merge only when some XCD splits its leftover units (the same test as the
   // kernels'); the grid covers the largest leftover count of any XCD

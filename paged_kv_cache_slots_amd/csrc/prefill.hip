@@ -515,6 +515,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const uint8_t* vt = vcomp(t);
         const int s16 = lane & 15;
         const int dh = (lane >> 4) & 1;
+        if constexpr (kFp8) {
+          // fp8 pools: the operands of one 16-key half at a time, the second
+          // half's reads under the first half's MFMAs (16 registers in flight
+          // instead of 32: fewer spills, measured 1 % faster; the bf16
+          // kernel, which does not spill, was 2.6 % slower this way)
+#pragma unroll
+          for (int mu = 0; mu < 2; ++mu) {
+            u32x2 lo[DB], hi[DB];
+            const int r = 32 * kh + 16 * mu + 4 * hf + (s16 >> 2);
+            const uint8_t* rowp = vt + r * S::ROWB + 8 * (s16 & 1);
+            const int sw = swz_v<D>(r);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+              const uint8_t* a0 = rowp + (((4 * d + 2 * dh + ((s16 & 3) >> 1)) ^ sw) << 4);
+              lo[d] = lds_read_tr(a0);
+              hi[d] = lds_read_tr(a0 + 8 * S::ROWB);
+            }
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+              o[d] = mfma32x32x16_bf16(u32x4{lo[d][0], lo[d][1], hi[d][0], hi[d][1]}, pk[mu], o[d]);
+          }
+          return;
+        }
         u32x2 lo[2][DB], hi[2][DB];
 #pragma unroll
         for (int mu = 0; mu < 2; ++mu) {

@@ -33,7 +33,7 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
             "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged",
-            "pkv_set_timing_events"]
+            "pkv_set_timing_events", "pkv_xcd_ids"]
 
 
 class PkvError(RuntimeError):
@@ -91,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                                 P]),
         "pkv_merge_states": (ctypes.c_int, [P, P, I32, I64, I32, I32, P, ctypes.c_int, P, P]),
         "pkv_set_timing_events": (None, [P, P]),
+        "pkv_xcd_ids": (ctypes.c_int, [P, I32, I32, P]),
         "pkv_rotate_rows": (ctypes.c_int, [P, I64, I64, I64, I32, I64, P]),
         "pkv_copy_slots": (ctypes.c_int, [PP, I32, I64, P, P, I64, P]),
         "pkv_causal_layout_bounds": (ctypes.c_int, [I32, I64, I64, P, I32, ctypes.POINTER(PkvCausalBounds)]),
@@ -421,6 +422,16 @@ def pkv_check_slots(pool: Pool, slots: torch.Tensor, stream=None) -> torch.Tenso
     _check("pkv_check_slots", load_library().pkv_check_slots(ctypes.byref(ps), slots.data_ptr(), slots.numel(),
                                                              bad.data_ptr(), _stream(stream)))
     return bad
+
+
+def pkv_xcd_ids(num_workgroups: int, threads: int = 64, device: str = "cuda:0", stream=None) -> torch.Tensor:
+    """Device int32 tensor [num_workgroups]: the XCC_ID hardware register
+    (the XCD in its low 4 bits) each workgroup of a launch of that shape ran
+    on.  Asynchronous; read it after a sync."""
+    out = torch.empty(max(0, int(num_workgroups)), dtype=torch.int32, device=device)
+    _check("pkv_xcd_ids", load_library().pkv_xcd_ids(out.data_ptr() if out.numel() else None, int(num_workgroups),
+                                                     int(threads), _stream(stream)))
+    return out
 
 
 def pkv_check_tables(pool: Pool, block_table: torch.Tensor, kv_lens: torch.Tensor, stream=None) -> torch.Tensor:

@@ -30,7 +30,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source flags.  The prefill kernel runs one wave per SIMD with the whole
+# Per-source flags.  The prefill kernel runs two waves per SIMD with the whole
 # softmax state in registers; MFMA results feed vector ALU work every step, so
 # its MFMAs use the VGPR form (accumulators in VGPRs, never copied from AGPRs).
 SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -9,6 +9,11 @@
 // One workgroup walks the whole input (a debugging call, not a hot path):
 // every thread counts its share, the workgroup sums through LDS and thread 0
 // writes the total, so the result needs no zeroing and no atomics.
+//
+// Also here: the probe of where workgroups run.  The prefill's persistent
+// schedule gives the kv heads of XCD x to workgroups x, x + 8, ... on the
+// assumption that the dispatcher places workgroup i on XCD i mod 8; the probe
+// lets a test (or a caller) check that on the device at hand.
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -57,7 +62,19 @@ __global__ void __launch_bounds__(kCheckThreads) check_tables_kernel(const int32
   write_total(mine, bad);
 }
 
+// Workgroup i writes the XCC_ID hardware register (the XCD it runs on) of
+// its first wave to out[i].
+__global__ void xcd_ids_kernel(int32_t* out) {
+  const int v = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (31 << 11));   // hwreg(HW_REG_XCC_ID), all 32 bits
+  if (threadIdx.x == 0) out[blockIdx.x] = v;
+}
+
 }  // namespace
+
+hipError_t launch_xcd_ids(int32_t* out, int32_t num_workgroups, int32_t threads, hipStream_t stream) {
+  hipLaunchKernelGGL(xcd_ids_kernel, dim3((unsigned)num_workgroups), dim3((unsigned)threads), 0, stream, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t capacity, int32_t* bad, hipStream_t stream) {
   hipLaunchKernelGGL(check_slots_kernel, dim3(1), dim3(kCheckThreads), 0, stream, slots, n, capacity, bad);

@@ -720,6 +720,14 @@ pkv_status pkv_causal_layout(const int32_t* table, int32_t table_len, const int3
 }
 
 // ---------------------------------------------------------------------------
+pkv_status pkv_xcd_ids(int32_t* out, int32_t num_workgroups, int32_t threads, hipStream_t stream) {
+  if (num_workgroups < 0 || threads < 64 || threads > 1024 || threads % 64 != 0) return PKV_ERR_SHAPE;
+  if (num_workgroups == 0) return PKV_OK;
+  if (!out) return PKV_ERR_NULL;
+  if (!aligned(out, 4)) return PKV_ERR_ALIGN;
+  return launch_xcd_ids(out, num_workgroups, threads, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status pkv_check_slots(const pkv_pool* pool, const int64_t* slots, int64_t n, int32_t* bad, hipStream_t stream) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;

@@ -218,6 +218,7 @@ int prefill_tail_units(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t 
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);
 hipError_t launch_copy_slots(const CopySlotsParams& p, int vec_bytes, hipStream_t stream);
 hipError_t launch_causal_layout(const LayoutParams& p, hipStream_t stream);
+hipError_t launch_xcd_ids(int32_t* out, int32_t num_workgroups, int32_t threads, hipStream_t stream);
 hipError_t launch_check_slots(const int64_t* slots, int64_t n, int64_t capacity, int32_t* bad, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t stride, const int32_t* lens, int32_t rows,
                                int32_t page_shift, int64_t num_pages, int32_t* bad, hipStream_t stream);

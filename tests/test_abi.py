@@ -261,6 +261,19 @@ def test_check_calls_argument_checks():
     assert lib.pkv_check_tables(ctypes.byref(bad), A, 8, A, 4, A, None) == 2
 
 
+def test_xcd_probe_argument_checks():
+    """pkv_xcd_ids refuses bad launch shapes and pointers on the host (nothing
+    launched); an empty probe is OK with a NULL pointer."""
+    lib = pkv.load_library()
+    assert lib.pkv_xcd_ids(None, 0, 64, None) == 0
+    assert lib.pkv_xcd_ids(None, 8, 64, None) == 1
+    assert lib.pkv_xcd_ids(A, -1, 64, None) == 2
+    assert lib.pkv_xcd_ids(A, 8, 63, None) == 2
+    assert lib.pkv_xcd_ids(A, 8, 96, None) == 2
+    assert lib.pkv_xcd_ids(A, 8, 2048, None) == 2
+    assert lib.pkv_xcd_ids(A + 2, 8, 64, None) == 6
+
+
 def _decode_noalloc(pool, **kw):
     a = dict(q=A, q_dtype=pkv.PKV_BF16, T=4, n=1, hq=32, table=A, tstride=128, lens=A, maxlen=4096, scale=0.1,
              out=A, out_dtype=pkv.PKV_BF16, lse=None)

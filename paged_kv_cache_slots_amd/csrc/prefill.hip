@@ -39,9 +39,11 @@
 //     runs on 32x32x64 fp8 MFMAs straight from the raw K tile, with Q held
 //     as two e4m3 code sets per row (hi, and 16x the residual through the
 //     MFMA's 2^-4 block scale), so scores carry about 2^-8 relative error;
-//     the page's K scale and Q's row scale multiply the scores.  Each step
-//     widens the next V tile to bf16 in LDS (exactly) for the bf16 PV, whose
-//     P carries the page's V scale in its exponent.
+//     the page's K scale and Q's row scale multiply the scores.  Raw V tiles
+//     are fetched one tile further ahead than bf16 ones, so that each step
+//     widens (exactly) the V tile of the next step's PV into one of two bf16
+//     tiles with no barrier of its own: the step's barrier orders it.  P
+//     carries the page's V scale in its exponent.
 //   * Loads never branch: keys at or past the unit's last visible key re-read
 //     that key (finite; its score is masked, its P is exactly 0), so dead page
 //     slots and table entries past the last page never reach a product.
@@ -75,7 +77,8 @@ constexpr int kSlotFloats = 4 * 65 * 64;   // partial state: [row block][64 outp
 // LDS of one workgroup.  bf16 pools: the LDS-DMA writes the bf16 tiles the
 // MFMAs read, NST stages each of K and V.  fp8 pools: the LDS-DMA writes raw
 // fp8 tiles (NST stages each); the fp8 QK^T MFMAs read the raw K tiles, and
-// each step converts the V tile the next PV needs into one bf16 V tile.
+// each step widens one raw V tile into one of two bf16 V tiles, which the PV
+// of the next step reads.
 template <int D, bool kFp8>
 struct PSmem {
   static constexpr int ROWB = D * 2;              // bytes of one bf16 key row in LDS (no padding: XOR swizzle)
@@ -84,7 +87,7 @@ struct PSmem {
   static constexpr int CH = DROWB / 16;           // 16-byte chunks per DMA row
   static constexpr int DTB = kKT * DROWB;         // bytes of one DMA tile
   static constexpr int NST = 3;                   // DMA pipeline stages of each of K and V
-  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? TB : 0);   // K stages, V stages, bf16 V
+  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? 2 * TB : 0);   // K stages, V stages, 2 bf16 V
   static constexpr int RPI = 1024 / DROWB;        // rows written by one LDS-DMA instruction (64 lanes x 16 B)
   static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
   static_assert(RPI * IPW == 8, "a wave writes 8 rows of each tile");
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // DMA rings, and the V tile the PV MFMAs read (the ring's own for bf16 pools)
       auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::DTB; };
       auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::DTB; };
-      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB : vstage(t); };
+      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB + ((t - t0 + 1) & 1) * S::TB : vstage(t); };
       // fp8: widen one raw V tile into the bf16 V tile (swizzled as the bf16
       // DMA would have written it); thread tid owns 16 codes: row tid / CH,
       // columns 16 (tid % CH) .. + 15.  Codes convert exactly (scale 1).
@@ -581,15 +584,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       };
 
       // prologue: zeros into V(t0-1)'s stage (the first PV uses it with P = 0);
-      // K(t0), K(t0+1), V(t0) landed; K(t0+2) in flight; S(t0); a barrier
-      // before K(t0)'s stage is refilled with K(t0+3)
+      // K(t0), K(t0+1), V(t0) landed; K(t0+2) in flight (fp8: V(t0+1) too,
+      // and V(t0-1)'s zeros widened); S(t0); a barrier before K(t0)'s stage is
+      // refilled with K(t0+3)
       const bool need_refresh = ((t1 * kKT - 1) >> shift) - page_base >= kTableCache;
       dma_tile(vpool_b, vstage(t0 - 1), t1, false);
       dma_tile(kpool_b, kstage(t0), t0, true);
       dma_tile(kpool_b, kstage(t0 + 1), t0 + 1, true);
       dma_tile(vpool_b, vstage(t0), t0, false);
       dma_tile(kpool_b, kstage(t0 + 2), t0 + 2, true);
-      wait_dma_and_barrier<S::IPW>();
+      if constexpr (kFp8) {
+        dma_tile(vpool_b, vstage(t0 + 1), t0 + 1, false);
+        wait_dma_and_barrier<2 * S::IPW>();
+        widen(vstage(t0 - 1), vcomp(t0 - 1));
+      } else {
+        wait_dma_and_barrier<S::IPW>();
+      }
       f32x16 sA, sB;
       u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
       qk(t0, sA);
@@ -600,11 +610,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // segment); PV of tile t-1 (P = 0 before the first); max of S(t+1).
       // s_cur / p_cur and s_next / p_prev trade roles between iterations.
       auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked) {
-        // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight
-        if constexpr (kFp8) {
-          widen(vstage(t - 1), vcomp(t - 1));
-          __syncthreads();
-        }
+        // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight.  fp8:
+        // raw V(t) landed and V(t-1) widened; widen V(t) into the bf16 tile
+        // that PV(t-2) read last step (this step's barrier orders it before
+        // PV(t) in the next step); V(t+1) in flight
+        if constexpr (kFp8) widen(vstage(t), vcomp(t));
         if (need_refresh) {
           const int last_t = t + 3 < t1 ? t + 3 : t1 - 1;
           if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) {
@@ -613,9 +623,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           }
         }
         if (t + 3 >= tw0 + 64) load_window(t);
-        // refill: K(t+3) into K(t)'s stage, V(t+1) into V(t-2)'s stage
+        // refill: K(t+3) into K(t)'s stage; V(t+1) into V(t-2)'s stage (fp8:
+        // V(t+2) into V(t-1)'s, whose raw codes were widened last step)
         dma_tile(kpool_b, kstage(t + 3), t + 3, true);
-        dma_tile(vpool_b, vstage(t + 1), t + 1, false);
+        if constexpr (kFp8) dma_tile(vpool_b, vstage(t + 2), t + 2, false);
+        else dma_tile(vpool_b, vstage(t + 1), t + 1, false);
         // lazy rescale: the offset of a row moves only when its max grows by
         // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
         const ScaleCache sct = tile_scales(t);   // tile t's page stays cached across a refresh
@@ -661,7 +673,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         pv(t - 1, p_prev);
         if constexpr (!kFp8) __builtin_amdgcn_s_setprio(0);
         mt = mask_max(s_next, t + 1, masked);
-        // K(t+2) and V(t) have landed once only this iteration's loads remain
+        // K(t+2) and V(t) (fp8: V(t+1)) have landed once only this
+        // iteration's loads remain
         wait_dma_and_barrier<2 * S::IPW>();
       };
       // iteration t masks tile t+1: this wave's keys up to 64 t + 96 + 32 kh - 1.
@@ -684,12 +697,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         pB[0] = pA[0];
         pB[1] = pA[1];
       }
-      // PV of the last tile (its P is in pB), then drain the trailing
-      // zero-range loads before the stages are reused
-      if constexpr (kFp8) {
-        widen(vstage(t1 - 1), vcomp(t1 - 1));
-        __syncthreads();
-      }
+      // PV of the last tile (its P is in pB; fp8: V(t1-1) widened in the last
+      // step), then drain the trailing zero-range loads before the stages
+      // are reused
       pv(t1 - 1, pB);
       wait_dma_and_barrier<0>();
     }

@@ -581,11 +581,13 @@ pkv_status pkv_check_tables(const pkv_pool* pool, const int32_t* block_table, in
  * multiple of 64) on stream; workgroup i writes the XCC_ID hardware register
  * of the XCD (accelerator complex die) it ran on to out[i] (device int32,
  * overwritten; the die index is in the low 4 bits).  The prefill's persistent
- * schedule (pkv_attn_prefill_block_causal) hands the kv heads of XCD x to
+ * schedule (pkv_attn_prefill_block_causal) hands the kv heads of group x to
  * workgroups x, x + 8, x + 16, ... so that each K/V tile is fetched once into
- * that XCD's L2; it assumes the dispatcher places workgroup i on XCD i mod 8,
- * which this probe checks for a given launch shape.  Results are correct
- * whatever the placement; only the L2 reuse depends on it.
+ * one XCD's L2; it assumes that workgroups whose ids agree mod 8 run on one
+ * XCD (the dispatcher deals them to the 8 XCDs round robin, starting where
+ * earlier launches left off), which this probe checks for a given launch
+ * shape.  Results are correct whatever the placement; only the L2 reuse
+ * depends on it.
  * Errors: NULL out with num_workgroups > 0 -> PKV_ERR_NULL; a bad size or
  * thread count -> PKV_ERR_SHAPE; out not 4-byte aligned -> PKV_ERR_ALIGN;
  * num_workgroups == 0 -> PKV_OK, nothing launched.

@@ -11,9 +11,10 @@
 // writes the total, so the result needs no zeroing and no atomics.
 //
 // Also here: the probe of where workgroups run.  The prefill's persistent
-// schedule gives the kv heads of XCD x to workgroups x, x + 8, ... on the
-// assumption that the dispatcher places workgroup i on XCD i mod 8; the probe
-// lets a test (or a caller) check that on the device at hand.
+// schedule gives the kv heads of group x to workgroups x, x + 8, ... on the
+// assumption that workgroups whose ids agree mod 8 run on one XCD (the
+// dispatcher deals workgroups to the XCDs round robin); the probe lets a test
+// (or a caller) check that on the device at hand.
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 

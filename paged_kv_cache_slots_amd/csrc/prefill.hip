@@ -47,10 +47,13 @@
 //   * Loads never branch: keys at or past the unit's last visible key re-read
 //     that key (finite; its score is masked, its P is exactly 0), so dead page
 //     slots and table entries past the last page never reach a product.
-//   * Schedule: a persistent grid, one 8-wave workgroup per CU.  Each XCD
-//     (workgroup id mod 8) owns whole kv heads; its workgroups first run whole
-//     units in rounds, all in lockstep along the keys, so every K/V tile of a
-//     head is fetched once into the XCD's L2 and reused by all of its q-tiles.
+//   * Schedule: a persistent grid, one 8-wave workgroup per CU.  The
+//     dispatcher deals workgroups to the 8 XCDs round robin (from an XCD that
+//     depends on earlier launches), so the workgroups whose ids agree mod 8
+//     share one XCD.  Each such group owns whole kv heads; its workgroups
+//     first run whole units in rounds, all in lockstep along the keys, so
+//     every K/V tile of a head is fetched once into the XCD's L2 and reused by
+//     all of its q-tiles.
 //     The units left over after the last full round (fewer than the XCD's
 //     workgroups) are split evenly along the keys over all of them (stream-K,
 //     with a workspace): a unit cut into pieces leaves normalised partial

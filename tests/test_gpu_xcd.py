@@ -1,13 +1,16 @@
 """Where the dispatcher places workgroups.
 
-The prefill's persistent schedule hands the kv heads of XCD x to workgroups
-x, x + 8, x + 16, ... so that each K/V tile of a head is fetched once into that
-XCD's L2 and reused by all the q-tiles there.  That assumes workgroup i runs on
-XCD i mod 8.  The probe reads each workgroup's XCC_ID hardware register; these
-tests check the assumption for the prefill's own launch shape (one 512-thread
-workgroup per CU, rounded down to a multiple of 8) and for a grid many times
-the CU count.  Correctness never depends on the placement; only the L2 reuse
-does."""
+The prefill's persistent schedule gives the kv heads of group x to workgroups
+x, x + 8, x + 16, ... so that each K/V tile of a head is fetched once into one
+XCD's L2 and reused by all the q-tiles there.  That needs the workgroups whose
+ids agree mod 8 to run on one XCD.  The dispatcher deals workgroups to the 8
+XCDs round robin; which XCD receives workgroup 0 depends on the launches
+before (seen on this chip: XCD 0 in a fresh process, XCD 7 after other
+kernels), which the grouping does not care about.  The probe reads each
+workgroup's XCC_ID hardware register; these tests check the grouping for the
+prefill's own launch shape (one 512-thread workgroup per CU, rounded down to a
+multiple of 8) and for a grid many times the CU count.  Correctness never
+depends on the placement; only the L2 reuse does."""
 
 import numpy as np
 import pytest
@@ -24,7 +27,7 @@ def _cus():
 
 
 @pytest.mark.parametrize("shape", ["prefill_grid", "many_small"])
-def test_workgroup_i_runs_on_xcd_i_mod_8(shape):
+def test_workgroups_agreeing_mod_8_share_an_xcd(shape):
     cus = _cus()
     if shape == "prefill_grid":
         n, threads = max(8, min(cus, 512) // 8 * 8), 512
@@ -34,7 +37,8 @@ def test_workgroup_i_runs_on_xcd_i_mod_8(shape):
     ids = pkv.pkv_xcd_ids(n, threads)
     torch.cuda.synchronize()
     xcd = ids.cpu().numpy() & 0xF
-    want = np.arange(n) % 8
-    # every die is used, and each workgroup sits on die (id mod 8)
-    assert sorted(set(xcd.tolist())) == list(range(8)), f"dies seen: {sorted(set(xcd.tolist()))}"
-    assert np.array_equal(xcd, want), f"{int((xcd != want).sum())} of {n} workgroups off their die"
+    # workgroups 0..7 land on 8 distinct dies, and every workgroup shares the
+    # die of the one among 0..7 its id agrees with mod 8
+    assert sorted(xcd[:8].tolist()) == list(range(8)), f"dies of workgroups 0..7: {xcd[:8].tolist()}"
+    want = xcd[np.arange(n) % 8]
+    assert np.array_equal(xcd, want), f"{int((xcd != want).sum())} of {n} workgroups off their group's die"

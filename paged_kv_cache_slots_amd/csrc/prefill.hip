@@ -669,8 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         else l += psum;
         // bf16: the wave issuing its MFMA chains takes issue priority, so the
         // other wave of the SIMD fills the vector pipe meanwhile (measured
-        // 1.3 % faster; the fp8 kernel, with its extra widening barrier, was
-        // 1 % slower with it)
+        // 1.3 % faster; the fp8 kernel measured the same with it or without)
         if constexpr (!kFp8) __builtin_amdgcn_s_setprio(1);
         qk(t + 1, s_next);
         pv(t - 1, p_prev);

@@ -157,6 +157,8 @@ DECODE_CASES = [
     ("rows80_ps32", [300, 1025], 8, 2, 64, 32, 20, "bf16"),       # R = 80: row groups
     ("fp8_gqa8_d128", EDGE_LENS, 64, 8, 128, 32, 1, "fp8"),
     ("fp8_d64_ps16", [1, 17, 33, 700], 8, 4, 64, 16, 1, "fp8"),
+    ("gqa4_ps128", [1, 127, 128, 129, 1000], 32, 8, 128, 128, 1, "bf16"),
+    ("fp8_ps256", [1, 255, 256, 257, 2000], 64, 8, 128, 256, 1, "fp8"),
 ]
 
 

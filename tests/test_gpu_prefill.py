@@ -85,6 +85,8 @@ SMALL = [
     ("blocks_64_ps64", 2, 300, [300, 257], [640, 0], 4, 2, 64, 64, 64),
     ("no_context", 1, 129, [129], [0], 3, 3, 128, 32, 100),
     ("all_padding_batch", 2, 40, [0, 33], [12, 40], 2, 2, 128, 32, 8),
+    ("big_pages_ps128", 2, 200, [200, 190], [300, 700], 4, 2, 128, 128, 50),
+    ("pages_256_d64", 1, 300, [300], [1000], 2, 1, 64, 256, 0),
 ]
 
 
@@ -247,6 +249,7 @@ FP8 = [
     ("fp8_blocks_of_37_ps64", 1, 260, [250], [97], 2, 2, 128, 64, 37, 0),
     ("fp8_no_context_zero_scales", 1, 129, [129], [0], 3, 3, 128, 32, 100, 2),
     ("fp8_all_padding_batch", 2, 40, [0, 33], [12, 40], 2, 2, 128, 32, 8, 0),
+    ("fp8_big_pages_ps128", 1, 200, [200], [500], 4, 4, 128, 128, 64, 1),
 ]
 
 

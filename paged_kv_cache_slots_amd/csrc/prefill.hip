@@ -24,7 +24,8 @@
 //     through ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-dim
 //     block and gets it transposed), so staging never transposes.
 //   * K/V tiles go from HBM to LDS by LDS-DMA (buffer loads that write LDS
-//     directly, no staging registers), three stages each, two tiles ahead.
+//     directly, no staging registers), four stages each, two tiles ahead
+//     (a power of two, so a tile's stage is a mask rather than a modulo).
 //     Rows are XOR-swizzled in 16-byte chunks instead of padded (the DMA
 //     writes 1 KiB runs), keeping both operand read patterns conflict-free.
 //   * Software pipeline of a wave, per tile t: exp of S(t) -> P(t); QK^T of
@@ -89,7 +90,7 @@ struct PSmem {
   static constexpr int DROWB = kFp8 ? D : 2 * D;  // bytes of one key row as the LDS-DMA writes it
   static constexpr int CH = DROWB / 16;           // 16-byte chunks per DMA row
   static constexpr int DTB = kKT * DROWB;         // bytes of one DMA tile
-  static constexpr int NST = 3;                   // DMA pipeline stages of each of K and V
+  static constexpr int NST = 4;                   // DMA pipeline stages of each of K and V
   static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? 2 * TB : 0);   // K stages, V stages, 2 bf16 V
   static constexpr int RPI = 1024 / DROWB;        // rows written by one LDS-DMA instruction (64 lanes x 16 B)
   static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
@@ -588,8 +589,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
 
       // prologue: zeros into V(t0-1)'s stage (the first PV uses it with P = 0);
       // K(t0), K(t0+1), V(t0) landed; K(t0+2) in flight (fp8: V(t0+1) too,
-      // and V(t0-1)'s zeros widened); S(t0); a barrier before K(t0)'s stage is
-      // refilled with K(t0+3)
+      // and V(t0-1)'s zeros widened); S(t0); a barrier (with four stages the
+      // first step's refills go to stages no wave has read)
       const bool need_refresh = ((t1 * kKT - 1) >> shift) - page_base >= kTableCache;
       dma_tile(vpool_b, vstage(t0 - 1), t1, false);
       dma_tile(kpool_b, kstage(t0), t0, true);
@@ -626,8 +627,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           }
         }
         if (t + 3 >= tw0 + 64) load_window(t);
-        // refill: K(t+3) into K(t)'s stage; V(t+1) into V(t-2)'s stage (fp8:
-        // V(t+2) into V(t-1)'s, whose raw codes were widened last step)
+        // refill: K(t+3) into K(t-1)'s stage; V(t+1) into V(t-3)'s stage (fp8:
+        // V(t+2) into V(t-2)'s, whose raw codes were widened two steps ago)
         dma_tile(kpool_b, kstage(t + 3), t + 3, true);
         if constexpr (kFp8) dma_tile(vpool_b, vstage(t + 2), t + 2, false);
         else dma_tile(vpool_b, vstage(t + 1), t + 1, false);

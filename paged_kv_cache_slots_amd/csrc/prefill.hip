@@ -117,23 +117,24 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // One LDS-DMA instruction (buffer_load_dwordx4 ... lds): every lane copies 16
-// bytes at byte offset voff of the buffer [base, base + nbytes) to LDS address
-// dst + 16 * lane (base, nbytes and dst uniform); lanes outside the range write
-// zeros.  Issued from asm so that the compiler's own wait counting does not
+// bytes at byte offset voff of the buffer [base, base + nbytes) to LDS byte
+// address lds_dst + 16 * lane (base, nbytes and lds_dst uniform; lds_dst an
+// offset from the workgroup's LDS base, so no generic-to-LDS pointer
+// conversion and its null check per instruction); lanes outside the range
+// write zeros.  Issued from asm so that the compiler's own wait counting does not
 // see it: it would otherwise wait for every pending LDS-DMA before each LDS
 // read it cannot prove disjoint (all of them here, the stages being a ring).
 // Completion is waited for explicitly with wait_dma_and_barrier; extra
 // operations in flight can only make the compiler's own vmcnt waits longer.
 // No other code of this kernel uses M0.
-__device__ __forceinline__ void dma16(const uint8_t* base, int nbytes, uint8_t* dst, int voff) {
+__device__ __forceinline__ void dma16(const uint8_t* base, int nbytes, uint32_t lds_dst, int voff) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4_t d;
   d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
   d[2] = __builtin_amdgcn_readfirstlane(nbytes);
   d[3] = 0x00020000;
-  const int m0v = __builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(dst));
+  const int m0v = __builtin_amdgcn_readfirstlane((int)lds_dst);
   asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" ::"v"(voff), "s"(m0v), "s"(d)
                : "memory");
 }
@@ -290,6 +291,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   constexpr int KSTEPS = D / 16;   // k-steps of QK^T
   constexpr int DB = D / 32;       // 32-dim output blocks
   __shared__ __attribute__((aligned(16))) uint8_t smem[S::BYTES];
+  // LDS byte address of smem (the LDS-DMA destinations are offsets from it)
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   __shared__ int32_t pages[kTableCache];
   __shared__ ScaleCache scales[kFp8 ? kTableCache : 1];
   __shared__ int32_t tcum[kMaxTailUnits + 1];
@@ -458,7 +461,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         const int kmax1 = x.kmax - 1;
         int pg = 0;
         if (live) pg = __builtin_amdgcn_readlane(win, t - tw0);
-        const uint8_t* base = pool_b + (int64_t)pg * page_stride_b + head_off_b;
+        // (page ids are never negative: an unsigned product needs no sign extension)
+        const uint8_t* base = pool_b + (uint64_t)(uint32_t)pg * (uint64_t)page_stride_b + head_off_b;
 #pragma unroll
         for (int j = 0; j < S::IPW; ++j) {
           const int r0 = S::RPI * (wave * S::IPW + j);
@@ -466,7 +470,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           const int key = min(t * kKT + r, kmax1);
           const int cc = kFp8 ? (is_k ? (lane % S::CH) ^ swz_k8(r) : lane % S::CH)
                               : (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
-          dma16(base, live ? rec_bytes : 0, tile + r0 * S::DROWB, (key & pmask) * row_b + cc * 16);
+          dma16(base, live ? rec_bytes : 0, smem_lds + (uint32_t)(tile - smem) + r0 * S::DROWB,
+                (key & pmask) * row_b + cc * 16);
         }
       };
       // S^T of this wave's key half of K tile t: keys 32 kh + 8 (i / 4) + 4 hf + (i % 4)

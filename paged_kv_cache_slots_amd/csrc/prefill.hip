@@ -317,6 +317,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   const int64_t page_stride_b = p.page_stride * esz;
   const uint8_t* kpool_b = reinterpret_cast<const uint8_t*>(p.k_pool);
   const uint8_t* vpool_b = reinterpret_cast<const uint8_t*>(p.v_pool);
+  // A wave's LDS-DMA writes rows 8 wave .. 8 wave + 7 of each tile, 8
+  // consecutive keys of one page (page_size >= 16).  Lane part of the byte
+  // offset of DMA instruction j: its row i of the 8 times the row pitch plus
+  // its 16-byte chunk, placed by the row's LDS swizzle.
+  int koffs[S::IPW], voffs[S::IPW];
+#pragma unroll
+  for (int j = 0; j < S::IPW; ++j) {
+    const int r = S::RPI * (wave * S::IPW + j) + lane / S::CH;   // row of the tile
+    const int ck = kFp8 ? (lane % S::CH) ^ swz_k8(r) : (lane % S::CH) ^ swz_k<D>(r);
+    const int cv = kFp8 ? lane % S::CH : (lane % S::CH) ^ swz_v<D>(r);
+    koffs[j] = (r - 8 * wave) * row_b + ck * 16;
+    voffs[j] = (r - 8 * wave) * row_b + cv * 16;
+  }
 
   // one segment: tiles [t0, t1) of unit u (ut tiles in all); first_seg tells
   // which of the workgroup's two slots a partial state goes to.
@@ -419,13 +432,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       load_window(t0);
 
       // LDS-DMA of tile t of K or V into its stage: this wave writes rows
-      // 8 wave .. 8 wave + 7 (one page: page_size >= 16).  Keys past the unit's
-      // last visible key re-read that key (a finite row: its score is masked
-      // and its P is 0); tiles past the segment issue zero-range loads that
-      // only write zeros into a free stage, so every iteration has the same
-      // loads in flight.
+      // 8 wave .. 8 wave + 7, keys kw .. kw + 7 of one page.  The buffer starts
+      // at key kw's row and its range ends after the last key the segment
+      // reads, so rows of keys past the unit's last visible key or past the
+      // segment load zeros (a zero row is finite: its score is masked and its
+      // P is 0), and tiles past the segment write only zeros into a free
+      // stage: every iteration has the same loads in flight.
       const int64_t head_off_b = (int64_t)x.g * D * esz;
-      const int rec_bytes = ((1 << shift) - 1) * row_b + D * esz;
+      const int klim = min(x.kmax, t1 * kKT);   // keys the segment reads: [.., klim)
       // DMA rings, and the V tile the PV MFMAs read (the ring's own for bf16 pools)
       auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::DTB; };
       auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::DTB; };
@@ -457,22 +471,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         return ScaleCache{c, 0.f, 1.f};
       };
       auto dma_tile = [&](const uint8_t* pool_b, uint8_t* tile, int t, bool is_k) {
-        const bool live = t < t1;
-        const int kmax1 = x.kmax - 1;
-        int pg = 0;
-        if (live) pg = __builtin_amdgcn_readlane(win, t - tw0);
+        const int kw = t * kKT + 8 * wave;
+        // rows that hold keys the segment reads, clamped to 0..8 on the scalar
+        // unit (left to itself the compiler takes a vector med3, a vector
+        // multiply and a readfirstlane per tile)
+        int rows;
+        asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, 8" : "=s"(rows) : "s"(klim - kw) : "scc");
+        // the window's lane t - tw0 holds kw's page while the tile is live (a
+        // tile past the segment takes any cached page: it loads nothing)
+        const int pg = __builtin_amdgcn_readlane(win, (t - tw0) & 63);
         // (page ids are never negative: an unsigned product needs no sign extension)
-        const uint8_t* base = pool_b + (uint64_t)(uint32_t)pg * (uint64_t)page_stride_b + head_off_b;
+        const uint8_t* base = pool_b + (uint64_t)(uint32_t)pg * (uint64_t)page_stride_b + head_off_b +
+                              (uint32_t)((kw & pmask) * row_b);
 #pragma unroll
-        for (int j = 0; j < S::IPW; ++j) {
-          const int r0 = S::RPI * (wave * S::IPW + j);
-          const int r = r0 + lane / S::CH;
-          const int key = min(t * kKT + r, kmax1);
-          const int cc = kFp8 ? (is_k ? (lane % S::CH) ^ swz_k8(r) : lane % S::CH)
-                              : (lane % S::CH) ^ (is_k ? swz_k<D>(r) : swz_v<D>(r));
-          dma16(base, live ? rec_bytes : 0, smem_lds + (uint32_t)(tile - smem) + r0 * S::DROWB,
-                (key & pmask) * row_b + cc * 16);
-        }
+        for (int j = 0; j < S::IPW; ++j)
+          dma16(base, rows * row_b, smem_lds + (uint32_t)(tile - smem) + S::RPI * (wave * S::IPW + j) * S::DROWB,
+                is_k ? koffs[j] : voffs[j]);
       };
       // S^T of this wave's key half of K tile t: keys 32 kh + 8 (i / 4) + 4 hf + (i % 4)
       auto qk = [&](int t, f32x16& acc) {

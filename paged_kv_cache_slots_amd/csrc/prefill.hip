@@ -45,9 +45,10 @@
 //     widens (exactly) the V tile of the next step's PV into one of two bf16
 //     tiles with no barrier of its own: the step's barrier orders it.  P
 //     carries the page's V scale in its exponent.
-//   * Loads never branch: keys at or past the unit's last visible key re-read
-//     that key (finite; its score is masked, its P is exactly 0), so dead page
-//     slots and table entries past the last page never reach a product.
+//   * Loads never branch: rows of keys at or past the unit's last visible key
+//     fall outside the LDS-DMA buffer's range and load zeros (finite; the
+//     score is masked, P is exactly 0), so dead page slots and table entries
+//     past the last page never reach a product.
 //   * Schedule: a persistent grid, one 8-wave workgroup per CU.  The
 //     dispatcher deals workgroups to the 8 XCDs round robin (from an XCD that
 //     depends on earlier launches), so the workgroups whose ids agree mod 8

@@ -622,7 +622,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         wait_dma_and_barrier<2 * S::IPW>();
         widen(vstage(t0 - 1), vcomp(t0 - 1));
       } else {
-        wait_dma_and_barrier<S::IPW>();
+        // bf16: every load landed (a pair of steps starts with nothing in flight)
+        wait_dma_and_barrier<0>();
       }
       f32x16 sA, sB;
       u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
@@ -633,25 +634,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // iteration t: exp of S(t) -> P(t); QK^T of tile t+1 (zeros past the
       // segment); PV of tile t-1 (P = 0 before the first); max of S(t+1).
       // s_cur / p_cur and s_next / p_prev trade roles between iterations.
-      auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked) {
-        // invariant: K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight.  fp8:
-        // raw V(t) landed and V(t-1) widened; widen V(t) into the bf16 tile
-        // that PV(t-2) read last step (this step's barrier orders it before
-        // PV(t) in the next step); V(t+1) in flight
+      // bf16: steps run in pairs (t, t + 1), t - t0 even, with one barrier at
+      // the end of the pair.  The pair's first step refills K(t+3), K(t+4),
+      // V(t+1), V(t+2) into the stages of K(t-1), K(t), V(t-3), V(t-2), all
+      // last read before the previous pair's barrier; the pair reads K(t+1),
+      // K(t+2), V(t-1), V(t), which landed before it.  fp8 keeps a barrier per
+      // step (its V widening is ordered by it).
+      auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked,
+                      auto second) {
+        constexpr bool kSecond = decltype(second)::value;
+        constexpr int ahead = kFp8 ? 3 : 4;   // furthest tile this step's refill loads
+        // invariant (fp8): K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight; raw
+        // V(t) landed and V(t-1) widened; widen V(t) into the bf16 tile that
+        // PV(t-2) read last step (this step's barrier orders it before PV(t)
+        // in the next step); V(t+1) in flight
         if constexpr (kFp8) widen(vstage(t), vcomp(t));
-        if (need_refresh) {
-          const int last_t = t + 3 < t1 ? t + 3 : t1 - 1;
-          if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) {
-            cache_pages((t * kKT) >> shift);
-            load_window(t);
+        if (kFp8 || !kSecond) {
+          if (need_refresh) {
+            const int last_t = t + ahead < t1 ? t + ahead : t1 - 1;
+            if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) {
+              cache_pages((t * kKT) >> shift);
+              load_window(t);
+            }
+          }
+          if (t + ahead >= tw0 + 64) load_window(t);
+          // refill: K(t+3) into K(t-1)'s stage; fp8: V(t+2) into V(t-2)'s,
+          // whose raw codes were widened two steps ago; bf16: K(t+4), V(t+1),
+          // V(t+2) as above
+          dma_tile(kpool_b, kstage(t + 3), t + 3, true);
+          if constexpr (kFp8) {
+            dma_tile(vpool_b, vstage(t + 2), t + 2, false);
+          } else {
+            dma_tile(kpool_b, kstage(t + 4), t + 4, true);
+            dma_tile(vpool_b, vstage(t + 1), t + 1, false);
+            dma_tile(vpool_b, vstage(t + 2), t + 2, false);
           }
         }
-        if (t + 3 >= tw0 + 64) load_window(t);
-        // refill: K(t+3) into K(t-1)'s stage; V(t+1) into V(t-3)'s stage (fp8:
-        // V(t+2) into V(t-2)'s, whose raw codes were widened two steps ago)
-        dma_tile(kpool_b, kstage(t + 3), t + 3, true);
-        if constexpr (kFp8) dma_tile(vpool_b, vstage(t + 2), t + 2, false);
-        else dma_tile(vpool_b, vstage(t + 1), t + 1, false);
         // lazy rescale: the offset of a row moves only when its max grows by
         // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
         const ScaleCache sct = tile_scales(t);   // tile t's page stays cached across a refresh
@@ -688,35 +706,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
           }
         if constexpr (kFp8) l = fmaf(psum, sct.vinv, l);
         else l += psum;
-        // bf16: the wave issuing its MFMA chains takes issue priority, so the
-        // other wave of the SIMD fills the vector pipe meanwhile (measured
-        // 1.3 % faster; the fp8 kernel measured the same with it or without)
-        if constexpr (!kFp8) __builtin_amdgcn_s_setprio(1);
+        // (No issue priority: with one barrier per pair of steps the two waves
+        // of a SIMD drift into complementary phases by themselves; raising the
+        // priority of the wave issuing MFMAs, a gain with a barrier per step,
+        // measured 3.5 % slower here.)
         qk(t + 1, s_next);
         pv(t - 1, p_prev);
-        if constexpr (!kFp8) __builtin_amdgcn_s_setprio(0);
         mt = mask_max(s_next, t + 1, masked);
-        // K(t+2) and V(t) (fp8: V(t+1)) have landed once only this
-        // iteration's loads remain
-        wait_dma_and_barrier<2 * S::IPW>();
+        // fp8: K(t+2) and V(t+1) have landed once only this step's loads
+        // remain; bf16: at the end of a pair every load has landed
+        if constexpr (kFp8) wait_dma_and_barrier<2 * S::IPW>();
+        else if constexpr (kSecond) wait_dma_and_barrier<0>();
       };
       // iteration t masks tile t+1: this wave's keys up to 64 t + 96 + 32 kh - 1.
       // It needs no mask when they lie wholly below every row's key limit.
-      // (Waves may switch loops at different t: every step has one barrier.)
+      // (Waves may switch loops at different t: every pair of steps has the
+      // same barriers.)
       const int off = 96 + 32 * kh;
       int t_mask = wmin < off ? t0 : (wmin - off) / kKT + 1;   // first t with 64 t + off > wmin
       t_mask = t_mask < t0 ? t0 : (t_mask > t1 ? t1 : t_mask);
       int t = t0;
       for (; t + 1 < t_mask; t += 2) {
-        step(t, sA, sB, pA, pB, std::false_type{});
-        step(t + 1, sB, sA, pB, pA, std::false_type{});
+        step(t, sA, sB, pA, pB, std::false_type{}, std::false_type{});
+        step(t + 1, sB, sA, pB, pA, std::false_type{}, std::true_type{});
       }
       for (; t + 1 < t1; t += 2) {
-        step(t, sA, sB, pA, pB, std::true_type{});
-        step(t + 1, sB, sA, pB, pA, std::true_type{});
+        step(t, sA, sB, pA, pB, std::true_type{}, std::false_type{});
+        step(t + 1, sB, sA, pB, pA, std::true_type{}, std::true_type{});
       }
       if (t < t1) {
-        step(t, sA, sB, pA, pB, std::true_type{});
+        step(t, sA, sB, pA, pB, std::true_type{}, std::false_type{});
         pB[0] = pA[0];
         pB[1] = pA[1];
       }

@@ -40,11 +40,11 @@
 //     runs on 32x32x64 fp8 MFMAs straight from the raw K tile, with Q held
 //     as two e4m3 code sets per row (hi, and 16x the residual through the
 //     MFMA's 2^-4 block scale), so scores carry about 2^-8 relative error;
-//     the page's K scale and Q's row scale multiply the scores.  Raw V tiles
-//     are fetched one tile further ahead than bf16 ones, so that each step
-//     widens (exactly) the V tile of the next step's PV into one of two bf16
-//     tiles with no barrier of its own: the step's barrier orders it.  P
-//     carries the page's V scale in its exponent.
+//     the page's K scale and Q's row scale multiply the scores.  PV stays on
+//     bf16 MFMAs: each operand is read from the raw V tile with one 8-bit
+//     transposed LDS read (8 codes of one dim per lane) and widened exactly
+//     in registers, so V costs half the LDS operand reads of a bf16 tile.
+//     P carries the page's V scale in its exponent.
 //   * Loads never branch: rows of keys at or past the unit's last visible key
 //     fall outside the LDS-DMA buffer's range and load zeros (finite; the
 //     score is masked, P is exactly 0), so dead page slots and table entries
@@ -79,11 +79,9 @@ constexpr int kThreads = 512;      // 8 waves, two per SIMD
 constexpr int kTableCache = 1024;  // page ids cached in LDS
 constexpr int kSlotFloats = 4 * 65 * 64;   // partial state: [row block][64 outputs + lse][lane]
 
-// LDS of one workgroup.  bf16 pools: the LDS-DMA writes the bf16 tiles the
-// MFMAs read, NST stages each of K and V.  fp8 pools: the LDS-DMA writes raw
-// fp8 tiles (NST stages each); the fp8 QK^T MFMAs read the raw K tiles, and
-// each step widens one raw V tile into one of two bf16 V tiles, which the PV
-// of the next step reads.
+// LDS of one workgroup: NST stages each of K and V, as the LDS-DMA writes
+// them (bf16 rows, or raw fp8 rows that the MFMA operand reads take as they
+// are).
 template <int D, bool kFp8>
 struct PSmem {
   static constexpr int ROWB = D * 2;              // bytes of one bf16 key row in LDS (no padding: XOR swizzle)
@@ -92,11 +90,10 @@ struct PSmem {
   static constexpr int CH = DROWB / 16;           // 16-byte chunks per DMA row
   static constexpr int DTB = kKT * DROWB;         // bytes of one DMA tile
   static constexpr int NST = 4;                   // DMA pipeline stages of each of K and V
-  static constexpr int STAGES = 2 * NST * DTB + (kFp8 ? 2 * TB : 0);   // K stages, V stages, 2 bf16 V
+  static constexpr int STAGES = 2 * NST * DTB;   // K stages, V stages
   static constexpr int RPI = 1024 / DROWB;        // rows written by one LDS-DMA instruction (64 lanes x 16 B)
   static constexpr int IPW = kKT / RPI / 8;       // DMA instructions per wave per tile, for each of K and V
   static_assert(RPI * IPW == 8, "a wave writes 8 rows of each tile");
-  static_assert(!kFp8 || kKT * CH == kThreads, "one 16-byte fp8 chunk of the V tile per thread");
   static constexpr int COMBINE = 4 * 66 * 64 * 4;   // key-half join: [row block][64 + 2 values][lane] floats
   static constexpr int BYTES = STAGES > COMBINE ? STAGES : COMBINE;
 };
@@ -174,6 +171,16 @@ typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* ptr) {
   const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_v4i16_ptr)((__attribute__((address_space(3))) uint8_t*)(ptr)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+// Transposed 8-byte LDS read of bytes (ds_read_b64_tr_b8): within each
+// 16-lane group, lane o receives byte (o % 8) of the 8-byte rows addressed by
+// lanes o / 8 + 2 i, i = 0..7, as its byte i (checked on the device).
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* ptr) {
+  const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i32*)((__attribute__((address_space(3))) uint8_t*)(ptr)));
   return __builtin_bit_cast(u32x2, r);
 }
 
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
   for (int j = 0; j < S::IPW; ++j) {
     const int r = S::RPI * (wave * S::IPW + j) + lane / S::CH;   // row of the tile
     const int ck = kFp8 ? (lane % S::CH) ^ swz_k8(r) : (lane % S::CH) ^ swz_k<D>(r);
-    const int cv = kFp8 ? lane % S::CH : (lane % S::CH) ^ swz_v<D>(r);
+    const int cv = kFp8 ? (lane % S::CH) ^ swz_k8(r) : (lane % S::CH) ^ swz_v<D>(r);
     koffs[j] = (r - 8 * wave) * row_b + ck * 16;
     voffs[j] = (r - 8 * wave) * row_b + cv * 16;
   }
@@ -441,29 +448,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // stage: every iteration has the same loads in flight.
       const int64_t head_off_b = (int64_t)x.g * D * esz;
       const int klim = min(x.kmax, t1 * kKT);   // keys the segment reads: [.., klim)
-      // DMA rings, and the V tile the PV MFMAs read (the ring's own for bf16 pools)
+      // DMA rings
       auto kstage = [&](int t) { return smem + ((t - t0 + S::NST) % S::NST) * S::DTB; };
       auto vstage = [&](int t) { return smem + (S::NST + (t - t0 + S::NST) % S::NST) * S::DTB; };
-      auto vcomp = [&](int t) { return kFp8 ? smem + 2 * S::NST * S::DTB + ((t - t0 + 1) & 1) * S::TB : vstage(t); };
-      // fp8: widen one raw V tile into the bf16 V tile (swizzled as the bf16
-      // DMA would have written it); thread tid owns 16 codes: row tid / CH,
-      // columns 16 (tid % CH) .. + 15.  Codes convert exactly (scale 1).
-      auto widen = [&](const uint8_t* raw, uint8_t* bf) {
-        if constexpr (kFp8) {
-          const int r = tid / S::CH, cc = tid % S::CH;
-          const u32x4 w = *reinterpret_cast<const u32x4*>(raw + r * S::DROWB + 16 * cc);
-          uint32_t h[8];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            h[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, false));
-            h[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, true));
-          }
-          const int sw = swz_v<D>(r);
-          uint8_t* row = bf + r * S::ROWB;
-          *reinterpret_cast<u32x4*>(row + (((2 * cc) ^ sw) << 4)) = u32x4{h[0], h[1], h[2], h[3]};
-          *reinterpret_cast<u32x4*>(row + (((2 * cc + 1) ^ sw) << 4)) = u32x4{h[4], h[5], h[6], h[7]};
-        }
-      };
       // scales of this wave's key half of tile t (fp8; the half is one page).
       // A half wholly past the unit's last key (all its scores masked) takes
       // the last key's page, which is cached: its scale must be finite.
@@ -539,29 +526,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // group (hf, dh) reads rows 32 kh + 16 mu + 4 hf + 0..3 (and + 8) of dims
       // 32 d + 16 dh .. + 15, transposed.
       auto pv = [&](int t, const u32x4 (&pk)[2]) {
-        const uint8_t* vt = vcomp(t);
+        const uint8_t* vt = vstage(t);
         const int s16 = lane & 15;
         const int dh = (lane >> 4) & 1;
         if constexpr (kFp8) {
-          // fp8 pools: the operands of one 16-key half at a time, the second
-          // half's reads under the first half's MFMAs (16 registers in flight
-          // instead of 32: fewer spills, measured 1 % faster; the bf16
-          // kernel, which does not spill, was 2.6 % slower this way)
+          // fp8 pools: one 8-bit transposed read per MFMA from the raw tile
+          // (rows of D codes, 16-byte chunks swizzled by swz_k8).  Lane j of
+          // 16-lane group g addresses key 32 kh + 16 mu + 8 (j / 8) + 4 (g / 2)
+          // + (j / 2) % 4, dims 32 d + 16 (g % 2) + 8 (j % 2) .. + 7, so lane l
+          // receives dim 32 d + l % 32 of the 8 keys of pk's order; the codes
+          // widen exactly (scale 1) to the bf16 A operand.
+          const int g = lane >> 4;
 #pragma unroll
           for (int mu = 0; mu < 2; ++mu) {
-            u32x2 lo[DB], hi[DB];
-            const int r = 32 * kh + 16 * mu + 4 * hf + (s16 >> 2);
-            const uint8_t* rowp = vt + r * S::ROWB + 8 * (s16 & 1);
-            const int sw = swz_v<D>(r);
+            const int key = 32 * kh + 16 * mu + 8 * (s16 >> 3) + 4 * (g >> 1) + ((s16 >> 1) & 3);
+            const uint8_t* rowp = vt + key * S::DROWB + 8 * (s16 & 1);
+            const int sw = swz_k8(key);
+            u32x2 raw[DB];
+#pragma unroll
+            for (int d = 0; d < DB; ++d) raw[d] = lds_read_tr8(rowp + (((2 * d + (g & 1)) ^ sw) << 4));
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
-              const uint8_t* a0 = rowp + (((4 * d + 2 * dh + ((s16 & 3) >> 1)) ^ sw) << 4);
-              lo[d] = lds_read_tr(a0);
-              hi[d] = lds_read_tr(a0 + 8 * S::ROWB);
+              const u32x4 a{
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d][0], 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d][0], 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d][1], 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d][1], 1.0f, true))};
+              o[d] = mfma32x32x16_bf16(a, pk[mu], o[d]);
             }
-#pragma unroll
-            for (int d = 0; d < DB; ++d)
-              o[d] = mfma32x32x16_bf16(u32x4{lo[d][0], lo[d][1], hi[d][0], hi[d][1]}, pk[mu], o[d]);
           }
           return;
         }
@@ -608,23 +600,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       };
 
       // prologue: zeros into V(t0-1)'s stage (the first PV uses it with P = 0);
-      // K(t0), K(t0+1), V(t0) landed; K(t0+2) in flight (fp8: V(t0+1) too,
-      // and V(t0-1)'s zeros widened); S(t0); a barrier (with four stages the
-      // first step's refills go to stages no wave has read)
+      // K(t0), K(t0+1), K(t0+2), V(t0) landed (a pair of steps starts with
+      // nothing in flight); S(t0); a barrier (with four stages the first
+      // pair's refills go to stages no wave has read or will read before it)
       const bool need_refresh = ((t1 * kKT - 1) >> shift) - page_base >= kTableCache;
       dma_tile(vpool_b, vstage(t0 - 1), t1, false);
       dma_tile(kpool_b, kstage(t0), t0, true);
       dma_tile(kpool_b, kstage(t0 + 1), t0 + 1, true);
       dma_tile(vpool_b, vstage(t0), t0, false);
       dma_tile(kpool_b, kstage(t0 + 2), t0 + 2, true);
-      if constexpr (kFp8) {
-        dma_tile(vpool_b, vstage(t0 + 1), t0 + 1, false);
-        wait_dma_and_barrier<2 * S::IPW>();
-        widen(vstage(t0 - 1), vcomp(t0 - 1));
-      } else {
-        // bf16: every load landed (a pair of steps starts with nothing in flight)
-        wait_dma_and_barrier<0>();
-      }
+      wait_dma_and_barrier<0>();
       f32x16 sA, sB;
       u32x4 pA[2], pB[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
       qk(t0, sA);
@@ -634,22 +619,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
       // iteration t: exp of S(t) -> P(t); QK^T of tile t+1 (zeros past the
       // segment); PV of tile t-1 (P = 0 before the first); max of S(t+1).
       // s_cur / p_cur and s_next / p_prev trade roles between iterations.
-      // bf16: steps run in pairs (t, t + 1), t - t0 even, with one barrier at
-      // the end of the pair.  The pair's first step refills K(t+3), K(t+4),
+      // Steps run in pairs (t, t + 1), t - t0 even, with one barrier at the
+      // end of the pair.  The pair's first step refills K(t+3), K(t+4),
       // V(t+1), V(t+2) into the stages of K(t-1), K(t), V(t-3), V(t-2), all
       // last read before the previous pair's barrier; the pair reads K(t+1),
-      // K(t+2), V(t-1), V(t), which landed before it.  fp8 keeps a barrier per
-      // step (its V widening is ordered by it).
+      // K(t+2), V(t-1), V(t), which landed before it.
       auto step = [&](int t, f32x16& s_cur, f32x16& s_next, u32x4 (&p_cur)[2], u32x4 (&p_prev)[2], auto masked,
                       auto second) {
         constexpr bool kSecond = decltype(second)::value;
-        constexpr int ahead = kFp8 ? 3 : 4;   // furthest tile this step's refill loads
-        // invariant (fp8): K(t+1), V(t-1) in LDS; K(t+2), V(t) in flight; raw
-        // V(t) landed and V(t-1) widened; widen V(t) into the bf16 tile that
-        // PV(t-2) read last step (this step's barrier orders it before PV(t)
-        // in the next step); V(t+1) in flight
-        if constexpr (kFp8) widen(vstage(t), vcomp(t));
-        if (kFp8 || !kSecond) {
+        constexpr int ahead = 4;   // furthest tile the pair's refill loads
+        if (!kSecond) {
           if (need_refresh) {
             const int last_t = t + ahead < t1 ? t + ahead : t1 - 1;
             if (((last_t * kKT + kKT - 1) >> shift) - page_base >= kTableCache) {
@@ -658,17 +637,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
             }
           }
           if (t + ahead >= tw0 + 64) load_window(t);
-          // refill: K(t+3) into K(t-1)'s stage; fp8: V(t+2) into V(t-2)'s,
-          // whose raw codes were widened two steps ago; bf16: K(t+4), V(t+1),
-          // V(t+2) as above
           dma_tile(kpool_b, kstage(t + 3), t + 3, true);
-          if constexpr (kFp8) {
-            dma_tile(vpool_b, vstage(t + 2), t + 2, false);
-          } else {
-            dma_tile(kpool_b, kstage(t + 4), t + 4, true);
-            dma_tile(vpool_b, vstage(t + 1), t + 1, false);
-            dma_tile(vpool_b, vstage(t + 2), t + 2, false);
-          }
+          dma_tile(kpool_b, kstage(t + 4), t + 4, true);
+          dma_tile(vpool_b, vstage(t + 1), t + 1, false);
+          dma_tile(vpool_b, vstage(t + 2), t + 2, false);
         }
         // lazy rescale: the offset of a row moves only when its max grows by
         // more than 8 (log2 units); P(t-1) is not yet in o, so it is rescaled too
@@ -713,10 +685,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         qk(t + 1, s_next);
         pv(t - 1, p_prev);
         mt = mask_max(s_next, t + 1, masked);
-        // fp8: K(t+2) and V(t+1) have landed once only this step's loads
-        // remain; bf16: at the end of a pair every load has landed
-        if constexpr (kFp8) wait_dma_and_barrier<2 * S::IPW>();
-        else if constexpr (kSecond) wait_dma_and_barrier<0>();
+        // at the end of a pair every load has landed
+        if constexpr (kSecond) wait_dma_and_barrier<0>();
       };
       // iteration t masks tile t+1: this wave's keys up to 64 t + 96 + 32 kh - 1.
       // It needs no mask when they lie wholly below every row's key limit.
@@ -739,9 +709,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams p) {
         pB[0] = pA[0];
         pB[1] = pA[1];
       }
-      // PV of the last tile (its P is in pB; fp8: V(t1-1) widened in the last
-      // step), then drain the trailing zero-range loads before the stages
-      // are reused
+      // PV of the last tile (its P is in pB), then drain the trailing
+      // zero-range loads before the stages are reused
       pv(t1 - 1, pB);
       wait_dma_and_barrier<0>();
     }

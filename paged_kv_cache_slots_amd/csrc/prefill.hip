@@ -177,7 +177,8 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* ptr) {
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 // Transposed 8-byte LDS read of bytes (ds_read_b64_tr_b8): within each
 // 16-lane group, lane o receives byte (o % 8) of the 8-byte rows addressed by
-// lanes o / 8 + 2 i, i = 0..7, as its byte i (checked on the device).
+// lanes o / 8 + 2 i, i = 0..7, as its byte i.  (The fp8 prefill's PV rests on
+// this layout; its parity tests against the oracle cover every operand.)
 __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* ptr) {
   const v2i32 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
       (__attribute__((address_space(3))) v2i32*)((__attribute__((address_space(3))) uint8_t*)(ptr)));

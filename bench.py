@@ -5,10 +5,11 @@
 
 Prints ONE JSON line.  The headline workload is the bf16 GQA decode (64
 sequences, lengths uniform in [512, 4096], 32 q / 8 kv heads of 128, 32-token
-pages in a 16384-page pool): one step = slot scatter of the step's 64 new
-tokens + paged decode, inputs resident in HBM.  ``value`` is the step's
-algorithmic bytes (K/V of every valid token once per kv head, Q, O, the table
-entries and lengths read, the scattered rows) over the measured step time.
+pages in a 16384-page pool): one step = one ``pkv_attn_decode_append`` call,
+whose decode kernel writes the step's 64 new tokens into their slots and then
+attends, inputs resident in HBM.  ``value`` is the step's algorithmic bytes
+(K/V of every valid token once per kv head, Q, O, the table entries and
+lengths read, the new tokens read and written) over the measured step time.
 
 The other workloads (block-causal prefill, shared-prefix n-sample decode,
 long fp8 decode) are measured in the same run and reported under
@@ -261,13 +262,15 @@ def run_headline(args, torch, pkv, W):
     dev = setup_decode_case(case, torch, pkv)
     hkv, d = case.pool.num_kv_heads, case.pool.head_dim
     t, n, hq, _ = case.q.shape
+    # the step is one pkv_attn_decode_append call: its decode kernel reads the
+    # 64 new tokens' K and V and writes them into their slots, then attends
+    append_bytes = 2 * 2 * len(case.slots) * hkv * d * 2
     dec_bytes = decode_bytes(case.kv_lens, case.pool.page_size, hkv, d, 2, t * n, hq, 2, 2, False, False)
-    scat_bytes = 2 * 2 * len(case.slots) * hkv * d * 2 + len(case.slots) * 8
-    step_bytes = dec_bytes + scat_bytes
+    kern_bytes = dec_bytes + append_bytes
+    step_bytes = kern_bytes
     ev = []
 
     def step(record=False, kernel=False):
-        pkv.pkv_scatter_slots(dev["pool"], dev["new_k"], dev["new_v"], dev["slots"])
         if record:
             # a: before the call; b: after it.  With `kernel`, the library
             # launches the decode kernel with the pair (ks, ke), which take
@@ -280,8 +283,8 @@ def run_headline(args, torch, pkv, W):
             a.record()
             if kernel:
                 pkv.pkv_set_timing_events(ks, ke)
-        pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], case.max_kv_len, case.sm_scale,
-                            dev["out"], None, dev["ws"])
+        pkv.pkv_attn_decode_append(dev["pool"], dev["new_k"], dev["new_v"], dev["q"], dev["tables"], dev["lens"],
+                                   case.max_kv_len, case.sm_scale, dev["out"], None, dev["ws"])
         if record:
             if kernel:
                 pkv.pkv_set_timing_events(None, None)
@@ -324,23 +327,9 @@ def run_headline(args, torch, pkv, W):
         step(record=True, kernel=True)
     torch.cuda.synchronize()
     kern_ms = float(np.mean([ks.elapsed_time(ke) for _, (ks, ke), _ in ev]))
-    # the scatter's own latency, in steps of its own (outside the timed loop:
-    # an extra event inside it would lengthen every step)
-    sev = []
-    for _ in range(20):
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        pkv.pkv_scatter_slots(dev["pool"], dev["new_k"], dev["new_v"], dev["slots"])
-        s1.record()
-        sev.append((s0, s1))
-        pkv.pkv_attn_decode(dev["pool"], dev["q"], dev["tables"], dev["lens"], case.max_kv_len, case.sm_scale,
-                            dev["out"], None, dev["ws"])
-    torch.cuda.synchronize()
-    scat_ms = float(np.mean([a.elapsed_time(b) for a, b in sev]))
     flushed = time_events(torch, lambda: step(), 20, Flusher(torch))
-    return case, dict(step_bytes=step_bytes, dec_bytes=dec_bytes, ms_per_step=wall * 1e3, decode_ms=dec_ms,
-                      decode_kernel_ms=kern_ms,
-                      scatter_ms=scat_ms, scatter_bytes=scat_bytes, flushed_step_ms=flushed, parity=parity)
+    return case, dict(step_bytes=step_bytes, dec_bytes=kern_bytes, ms_per_step=wall * 1e3, decode_ms=dec_ms,
+                      decode_kernel_ms=kern_ms, append_bytes=append_bytes, flushed_step_ms=flushed, parity=parity)
 
 
 # ----------------------------------------------------------------------------- secondary workloads
@@ -862,25 +851,28 @@ def main():
         "ms_per_step": round(h["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "bf16 GQA paged decode: 64 sequences, lengths U[512,4096], 32 q / 8 kv heads x 128, "
-                               "32-token pages shuffled over a 16384-page pool; step = scatter of 64 new tokens + "
-                               "decode",
+                               "32-token pages shuffled over a 16384-page pool; step = one "
+                               "pkv_attn_decode_append call (the decode kernel writes the 64 new tokens into their "
+                               "slots, then attends)",
                    "global_batch": 64, "seq_len": int(case.max_kv_len), "total_keys": int(case.kv_lens.sum()),
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "kernel": "decode_skh_kernel (the dominant kernel of the pkv_attn_decode call)",
+                     "kernel": "decode_skh_kernel (the dominant kernel of the pkv_attn_decode_append call; it also "
+                               "writes the step's 64 tokens)",
                      "timing": "HIP events on the launch stream over --steps further steps (not inside the "
                                "wall-clock loop): the library launches the decode kernel through "
                                "hipExtLaunchKernel with a start / stop event pair, which take that kernel's own "
                                "start and end times (the merge kernel of the split units is outside the span)",
                      "bytes_per_launch": h["dec_bytes"], "avg_launch_ms": round(h["decode_kernel_ms"], 5),
-                     "call": {"what": "the whole pkv_attn_decode call: decode kernel + merge kernel of the split "
-                                      "units + the gap between them",
+                     "call": {"what": "the whole pkv_attn_decode_append call: decode kernel (with the token writes) + "
+                                      "merge kernel of the split units + the gap between them",
                               "avg_ms": round(h["decode_ms"], 5), "achieved": round(call_gbs, 1),
                               "frac": round(call_gbs / HBM_PEAK_GBS, 4)}},
         "parity": h["parity"],
-        "scatter": {"what": "the step's pkv_scatter_slots of 64 new tokens (latency-bound at this size)",
-                    "ms": round(h["scatter_ms"], 5), "bytes": h["scatter_bytes"]},
+        "append": {"what": "the step's 64 new tokens (K and V, 8 kv heads x 128): read and written into their "
+                           "slots by the decode kernel itself, before its own walk reads them (no scatter launch)",
+                   "bytes": h["append_bytes"]},
         "flushed_step_ms_median_p10_p90": [round(x, 5) for x in h["flushed_step_ms"]],
         "device": device_info(torch, pkv),
         "copy_ceiling": copy_ceiling(torch),

@@ -182,15 +182,16 @@ pkv_status pkv_attn_decode(const pkv_pool* pool, const void* q, pkv_dtype q_dtyp
 /*
  * pkv_set_timing_events -- measurement hook.  While start or stop is not
  * NULL, the main kernel of every pkv_attn_decode / pkv_attn_decode_noalloc /
- * pkv_attn_decode_step / prefill call (the stream-K, split or fp32 decode
- * kernel; the prefill kernel; not a merge kernel of split work) is launched
- * through hipExtLaunchKernel with these events, which then carry that
- * kernel's own start and end times: hipEventElapsedTime(start, stop) is the
- * kernel's duration, with no marker between it and its neighbours.  Each
- * such launch sets both events again, so after a call they hold its main
- * kernel's times.  NULL, NULL turns the hook off.  Process-wide and not
- * synchronised: set it while no other host thread calls the library.  The
- * events are the caller's, created before the call.
+ * pkv_attn_decode_step / pkv_attn_decode_append / prefill call (the
+ * stream-K, split or fp32 decode kernel; the prefill kernel; not a merge
+ * kernel of split work, nor the scatter that pkv_attn_decode_append may run
+ * first) is launched through hipExtLaunchKernel with these events, which
+ * then carry that kernel's own start and end times: hipEventElapsedTime(start,
+ * stop) is the kernel's duration, with no marker between it and its
+ * neighbours.  Each such launch sets both events again, so after a call they
+ * hold its main kernel's times.  NULL, NULL turns the hook off.  Process-wide
+ * and not synchronised: set it while no other host thread calls the library.
+ * The events are the caller's, created before the call.
  */
 void pkv_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
@@ -241,6 +242,41 @@ pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q
                                 int32_t max_kv_len, float sm_scale,
                                 void* out, pkv_dtype out_dtype, float* out_lse,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_attn_decode_append -- write a step's K/V into the cache and attend, in
+ * one call.
+ * [P5] FA4 tail commit (the step's K/V goes into the row's pages first, then
+ * is attended causally); "Paged causal K/V cache and cached attention for
+ * VisualGen", Description / Cache (the chunk's K/V written into its slots
+ * before attention).
+ *
+ * new_k, new_v: the step's tokens, element type of the pool, rows
+ * [num_tables * q_len, num_kv_heads, head_dim] with token stride
+ * new_tok_stride and kv-head stride new_head_stride (elements; the head_dim
+ * elements of a row contiguous).  Token j of table row t (row t * q_len + j)
+ * is logical key kv_lens[t] - q_len + j of that row: it is written, bytes
+ * untouched, into that key's slot (page block_table[t][key / page_size], row
+ * key % page_size), as pkv_scatter_slots would, and then every argument and
+ * result is that of pkv_attn_decode_step over the updated pool.  Tokens whose
+ * key would be negative (kv_lens[t] < q_len - j) are not written.  The slots
+ * written must belong to the call alone (no other row's key maps to them).
+ * With a stream-K workspace and kv heads in quads (one 16-row block per
+ * row: q_len * num_q_heads / num_kv_heads <= 16), 16-byte aligned new_k /
+ * new_v and strides, the decode kernel writes the tokens itself (no separate
+ * launch); otherwise a scatter kernel runs first.  Either way the pool holds
+ * the tokens when the call's work on the stream is done.
+ * Errors: NULL new_k or new_v -> PKV_ERR_NULL; negative strides ->
+ * PKV_ERR_SHAPE; the rest as pkv_attn_decode_step.
+ */
+pkv_status pkv_attn_decode_append(const pkv_pool* pool, const void* new_k, const void* new_v,
+                                  int64_t new_tok_stride, int64_t new_head_stride,
+                                  const void* q, pkv_dtype q_dtype,
+                                  int32_t num_tables, int32_t q_len, int32_t num_q_heads,
+                                  const int32_t* block_table, int32_t table_stride, const int32_t* kv_lens,
+                                  int32_t max_kv_len, float sm_scale,
+                                  void* out, pkv_dtype out_dtype, float* out_lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pkv_attn_decode_shared_prefix -- one n-sample decode step: shared prefix,

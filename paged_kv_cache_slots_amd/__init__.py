@@ -33,7 +33,7 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
             "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged",
-            "pkv_set_timing_events", "pkv_xcd_ids"]
+            "pkv_set_timing_events", "pkv_xcd_ids", "pkv_attn_decode_append"]
 
 
 class PkvError(RuntimeError):
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_decode_noalloc": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, P, I32, P, I32, F32, P,
                                                    ctypes.c_int, P, P]),
+        "pkv_attn_decode_append": (ctypes.c_int, [PP, P, P, I64, I64, P, ctypes.c_int, I32, I32, I32, P, I32, P,
+                                                  I32, F32, P, ctypes.c_int, P, P, SZ, P]),
         "pkv_attn_decode_shared_prefix_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_decode_shared_prefix": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, I32, P, I32, P, I32, P,
                                                          I32, P, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
@@ -222,6 +224,32 @@ def pkv_attn_decode_step(pool: Pool, q: torch.Tensor, block_table: torch.Tensor,
         ctypes.byref(ps), q.data_ptr(), _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(),
         block_table.stride(0), kv_lens.data_ptr(), int(max_kv_len), float(sm_scale), out.data_ptr(),
         _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_decode_append(pool: Pool, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
+                           block_table: torch.Tensor, kv_lens: torch.Tensor, max_kv_len: int, sm_scale: float,
+                           out: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write a step's K/V and attend: ``new_k`` / ``new_v`` [T * q_len, Hkv, D]
+    (or [T, q_len, Hkv, D]) in the pool's element type, rows of D contiguous;
+    token j of row t becomes key kv_lens[t] - q_len + j, then as
+    ``pkv_attn_decode_step`` with ``q`` [T, q_len, Hq, D]."""
+    if not q.is_contiguous() or not out.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("q, out and block_table must be contiguous")
+    t, n, hq, d = q.shape
+    hkv = pool.k.shape[-2]
+    nk, nv = new_k.reshape(-1, hkv, d), new_v.reshape(-1, hkv, d)
+    if nk.shape[0] != t * n or nv.shape != nk.shape or nk.stride() != nv.stride() or nk.stride(2) != 1:
+        raise ValueError("new_k / new_v must be [T * q_len, Hkv, D] with matching strides and contiguous rows")
+    if nk.element_size() != pool.k.element_size():
+        raise ValueError("new_k / new_v must have the pool's element type")
+    ps = pool.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_attn_decode_append", load_library().pkv_attn_decode_append(
+        ctypes.byref(ps), nk.data_ptr(), nv.data_ptr(), nk.stride(0), nk.stride(1), q.data_ptr(),
+        _dtype_code(q.dtype), t, n, hq, block_table.data_ptr(), block_table.stride(0), kv_lens.data_ptr(),
+        int(max_kv_len), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype), _ptr(out_lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def pkv_attn_decode_shared_prefix_workspace_bytes(groups: int, samples: int, q_len: int, num_q_heads: int,

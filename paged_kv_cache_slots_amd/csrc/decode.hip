@@ -302,10 +302,14 @@ __device__ __forceinline__ void reset_state(RowState<D>& st) {
 // head): windows of 64 tiles get their page ids (and fp8 scales) with one
 // vector load; inside a window every tile is prefetched one step ahead with
 // unconditional loads (zero-range descriptor past the window's end).
-template <int D, bool kFp8>
+// hook() runs once, just before the loads of tile hook_tile are issued.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <int D, bool kFp8, typename Hook = NoHook>
 __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
                                            const int32_t* trow, int g, int len, int lim, int lim_lo, int first,
-                                           int step, int n) {
+                                           int step, int n, int hook_tile = -1, Hook hook = Hook{}) {
   constexpr int esz = kFp8 ? 1 : 2;
   const int lane = threadIdx.x & 63;
   const int r_lane = lane & 15, j = lane >> 4;
@@ -325,6 +329,7 @@ __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D /
     auto issue = [&](TileRegs<D, kFp8>& X, int k) {
       const bool ok = k < n_win;
       const int kc = ok ? k : 0;
+      if (ok && first + (w0 + k) * step == hook_tile) hook();
       const int key0 = (first + (w0 + kc) * step) * 32;
       issue_tile<D, kFp8>(X, kp, vp, rl(win.e0, kc), rl(win.e1, kc), key0 & pmask, (key0 + 16) & pmask,
                           page_stride_b, head_off_b, row_b, ok ? page_bytes : 0, lo);
@@ -612,6 +617,32 @@ __global__ __launch_bounds__(256, 2) void shared_prefix_kernel(DecodeParams pre,
   }
 }
 
+// Write the step's tokens at keys [kb, ke) of table row t (key x is step
+// token x - (len - n)) for kv head g into the pool: 16 bytes per lane and
+// instruction, then wait until the stores have completed.
+template <int D, bool kFp8>
+__device__ __forceinline__ void append_rows(const DecodeParams& p, int t, int g, int len, int kb, int ke) {
+  constexpr int esz = kFp8 ? 1 : 2;
+  constexpr int CPR = D * esz / 16;   // 16-byte chunks per row
+  const int lane = threadIdx.x & 63;
+  const int n = p.rows_per_table;
+  const int row_b = p.num_kv_heads * D * esz;
+  const int64_t page_stride_b = p.page_stride * esz;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  uint8_t* kp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_pool));
+  uint8_t* vp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_pool));
+  for (int i = lane; i < (ke - kb) * CPR; i += 64) {
+    const int key = kb + i / CPR, c = i % CPR;
+    const int64_t src = (int64_t)(t * n + key - (len - n)) * p.new_tok_stride_b + (int64_t)g * p.new_head_stride_b + 16 * c;
+    const int64_t dst = (int64_t)trow[key >> p.page_shift] * page_stride_b + (int64_t)(key & pmask) * row_b +
+                        (int64_t)g * D * esz + 16 * c;
+    *reinterpret_cast<u32x4*>(kp + dst) = *reinterpret_cast<const u32x4*>(p.new_k + src);
+    *reinterpret_cast<u32x4*>(vp + dst) = *reinterpret_cast<const u32x4*>(p.new_v + src);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Head-parallel stream-K worker (units of one 16-row block; kv heads a
 // multiple of 4): a workgroup is one worker whose 4 waves take kv heads
 // 4 hg .. 4 hg + 3 of the same keys.  The flattened positions are (table row
@@ -661,8 +692,46 @@ __device__ __forceinline__ void decode_sk_heads(const DecodeParams& p, const int
     RowState<D> st;
     reset_state(st);
     const int len = p.kv_lens[t];
+    // The step's tokens (keys len - n .. len - 1) that fall in this
+    // segment's tiles: this wave writes its kv head's rows, and only its own
+    // walk reads them.  Up to 64 16-byte chunks (4 tokens of 128 bf16 dims)
+    // are loaded now, one per lane, and stored just before the walk issues
+    // the loads of the first tile that holds them, so the load latency hides
+    // under the tiles before it; the wave's later loads of those rows follow
+    // its stores in issue order.  More tokens are written before the walk.
+    constexpr int CPR = D * (kFp8 ? 1 : 2) / 16;   // 16-byte chunks per row
+    int hook_tile = -1;
+    u32x4 tok_k = {0u, 0u, 0u, 0u}, tok_v = {0u, 0u, 0u, 0u};
+    int64_t tok_dst = -1;
+    if (p.new_k) {
+      const int n = p.rows_per_table;
+      const int kb = max(len - n, k0 * 32), ke = min(len, k1 * 32);
+      if (kb < ke && (ke - kb) * CPR <= 64) {
+        if (lane < (ke - kb) * CPR) {
+          const int key = kb + lane / CPR, c = lane % CPR;
+          const int64_t src = (int64_t)(t * n + key - (len - n)) * p.new_tok_stride_b +
+                              (int64_t)g * p.new_head_stride_b + 16 * c;
+          tok_k = *reinterpret_cast<const u32x4*>(p.new_k + src);
+          tok_v = *reinterpret_cast<const u32x4*>(p.new_v + src);
+          const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+          tok_dst = (int64_t)trow[key >> p.page_shift] * p.page_stride * (kFp8 ? 1 : 2) +
+                    (int64_t)(key & ((1 << p.page_shift) - 1)) * p.num_kv_heads * D * (kFp8 ? 1 : 2) +
+                    (int64_t)g * D * (kFp8 ? 1 : 2) + 16 * c;
+        }
+        hook_tile = kb / 32;
+      } else if (kb < ke) {
+        append_rows<D, kFp8>(p, t, g, len, kb, ke);
+      }
+    }
+    auto store_tokens = [&]() {
+      if (tok_dst >= 0) {
+        *reinterpret_cast<u32x4*>(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_pool)) + tok_dst) = tok_k;
+        *reinterpret_cast<u32x4*>(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_pool)) + tok_dst) = tok_v;
+      }
+      asm volatile("" ::: "memory");
+    };
     walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                        row_limit(p, len, 0), k0, 1, k1 - k0);
+                        row_limit(p, len, 0), k0, 1, k1 - k0, hook_tile, store_tokens);
     st.l += __shfl_xor(st.l, 16, 64);
     st.l += __shfl_xor(st.l, 32, 64);
     const bool empty = st.l == 0.f;
@@ -1057,7 +1126,7 @@ int sk_waves_per_worker(int rows_per_unit) {
 template <int D, bool kFp8, int WR>
 static hipError_t launch_sk_dw(DecodeParams p, int sm_count, hipStream_t stream) {
   // one 16-row block per unit and kv heads in quads: head-parallel workgroups
-  p.head_par = (WR == 1 && p.row_groups == 1 && p.num_kv_heads % 4 == 0) ? 1 : 0;
+  p.head_par = sk_head_parallel(WR, p.row_groups, p.num_kv_heads) ? 1 : 0;
   // One workgroup per CU.  With two per CU the first-resident one wins issue
   // and ends early while the other runs on alone, so one per CU loses no
   // bandwidth and walks chunks twice as long, with half the cut pieces and

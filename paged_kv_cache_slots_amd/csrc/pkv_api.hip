@@ -157,14 +157,13 @@ const char* pkv_status_string(pkv_status s) {
 int32_t pkv_abi_version(void) { return kAbiVersion; }
 
 // ---------------------------------------------------------------------------
-pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void* src_v, int64_t src_tok_stride,
-                             int64_t src_head_stride, const int64_t* src_idx, const int64_t* slots,
-                             const int64_t* slots2, int64_t n_tokens, hipStream_t stream) {
-  pkv_status st = check_pool(pool);
-  if (st != PKV_OK) return st;
-  if (n_tokens < 0 || src_tok_stride < 0 || src_head_stride < 0) return PKV_ERR_SHAPE;
-  if (n_tokens == 0) return PKV_OK;   // empty tensors may carry NULL pointers
-  if (!src_k || !src_v || !slots) return PKV_ERR_NULL;
+// The scatter kernel over n_tokens rows, with explicit slots or (table !=
+// NULL) in append mode; the widest vector every operand's alignment allows.
+static hipError_t launch_scatter_rows(const pkv_pool* pool, const void* src_k, const void* src_v,
+                                      int64_t src_tok_stride, int64_t src_head_stride, const int64_t* src_idx,
+                                      const int64_t* slots, const int64_t* slots2, int64_t n_tokens,
+                                      const int32_t* table, const int32_t* lens, int32_t table_stride,
+                                      int32_t q_len, hipStream_t stream) {
   const int es = elem_bytes(pool->dtype);
   const int64_t row_b = (int64_t)pool->head_dim * es;
   int vec = 16;
@@ -183,6 +182,10 @@ pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void
   p.src_idx = src_idx;
   p.slots = slots;
   p.slots2 = slots2;
+  p.table = table;
+  p.lens = lens;
+  p.table_stride = table_stride;
+  p.q_len = q_len;
   p.n_tokens = n_tokens;
   p.src_tok_stride_b = src_tok_stride * es;
   p.src_head_stride_b = src_head_stride * es;
@@ -191,8 +194,23 @@ pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void
   p.page_shift = log2i(pool->page_size);
   p.num_kv_heads = pool->num_kv_heads;
   p.vecs_per_row = (int32_t)(row_b / vec);
-  return launch_scatter(p, vec, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_scatter(p, vec, stream);
 }
+
+pkv_status pkv_scatter_slots(const pkv_pool* pool, const void* src_k, const void* src_v, int64_t src_tok_stride,
+                             int64_t src_head_stride, const int64_t* src_idx, const int64_t* slots,
+                             const int64_t* slots2, int64_t n_tokens, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (n_tokens < 0 || src_tok_stride < 0 || src_head_stride < 0) return PKV_ERR_SHAPE;
+  if (n_tokens == 0) return PKV_OK;   // empty tensors may carry NULL pointers
+  if (!src_k || !src_v || !slots) return PKV_ERR_NULL;
+  return launch_scatter_rows(pool, src_k, src_v, src_tok_stride, src_head_stride, src_idx, slots, slots2, n_tokens,
+                             nullptr, nullptr, 0, 0, stream) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 
 // ---------------------------------------------------------------------------
 size_t pkv_attn_decode_workspace_bytes(int32_t num_tables, int32_t rows_per_table, int32_t num_q_heads,
@@ -215,9 +233,13 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
                               int32_t rows_per_table, int32_t num_q_heads, const int32_t* block_table,
                               int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
                               void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
-                              size_t workspace_bytes, int32_t causal, hipStream_t stream, bool scratch = false) {
+                              size_t workspace_bytes, int32_t causal, hipStream_t stream, bool scratch = false,
+                              const void* new_k = nullptr, const void* new_v = nullptr,
+                              int64_t new_tok_stride = 0, int64_t new_head_stride = 0) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
+  const bool append = new_k != nullptr || new_v != nullptr;
+  if (append && (new_tok_stride < 0 || new_head_stride < 0)) return PKV_ERR_SHAPE;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
   if (num_tables < 0 || rows_per_table < 1 || num_q_heads < 1 || table_stride < 1 || max_kv_len < 0 ||
       !(sm_scale > 0.f) || sm_scale > 3.0e38f)
@@ -226,6 +248,7 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   if ((int64_t)max_kv_len > (int64_t)table_stride * pool->page_size) return PKV_ERR_SHAPE;
   if (num_tables == 0) return PKV_OK;   // empty tensors may carry NULL pointers
   if (!q || !block_table || !kv_lens || !out) return PKV_ERR_NULL;
+  if (append && (!new_k || !new_v)) return PKV_ERR_NULL;
   const int D = pool->head_dim;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
@@ -284,6 +307,26 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   p.ws_o = nullptr;
   p.ws_lse = nullptr;
   p.ws_cum = nullptr;
+  p.new_k = nullptr;
+  p.new_v = nullptr;
+  p.new_tok_stride_b = 0;
+  p.new_head_stride_b = 0;
+  if (append) {
+    // the head-parallel stream-K kernel writes the step's tokens itself (16-byte
+    // rows and strides); every other path scatters them first, in append mode
+    const bool fused = use_sk && sk_head_parallel(sk_wr, sk_rg, pool->num_kv_heads) && aligned(new_k, 16) &&
+                       aligned(new_v, 16) && (new_tok_stride * es) % 16 == 0 && (new_head_stride * es) % 16 == 0;
+    if (fused) {
+      p.new_k = static_cast<const uint8_t*>(new_k);
+      p.new_v = static_cast<const uint8_t*>(new_v);
+      p.new_tok_stride_b = new_tok_stride * es;
+      p.new_head_stride_b = new_head_stride * es;
+    } else if (launch_scatter_rows(pool, new_k, new_v, new_tok_stride, new_head_stride, nullptr, nullptr, nullptr,
+                                   (int64_t)num_tables * rows_per_table, block_table, kv_lens, table_stride,
+                                   rows_per_table, stream) != hipSuccess) {
+      return PKV_ERR_HIP;
+    }
+  }
   if (use_sk) {
     uint8_t* w = static_cast<uint8_t*>(workspace);
     p.ws_cum = reinterpret_cast<int32_t*>(w);
@@ -412,6 +455,10 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
   pre.ws_o = ws_o;
   pre.ws_lse = ws_lse;
   pre.ws_cum = nullptr;
+  pre.new_k = nullptr;
+  pre.new_v = nullptr;
+  pre.new_tok_stride_b = 0;
+  pre.new_head_stride_b = 0;
   pre.page_stride = pool->page_stride;
   pre.page_shift = log2i(pool->page_size);
   pre.num_kv_heads = pool->num_kv_heads;
@@ -466,6 +513,21 @@ pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q
                                 size_t workspace_bytes, hipStream_t stream) {
   return decode_call(pool, q, q_dtype, num_tables, q_len, num_q_heads, block_table, table_stride, kv_lens,
                      max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 1, stream);
+}
+
+pkv_status pkv_attn_decode_append(const pkv_pool* pool, const void* new_k, const void* new_v,
+                                  int64_t new_tok_stride, int64_t new_head_stride, const void* q, pkv_dtype q_dtype,
+                                  int32_t num_tables, int32_t q_len, int32_t num_q_heads, const int32_t* block_table,
+                                  int32_t table_stride, const int32_t* kv_lens, int32_t max_kv_len, float sm_scale,
+                                  void* out, pkv_dtype out_dtype, float* out_lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (num_tables > 0 && !new_k && !new_v) {   // (one of the two NULL is caught by decode_call)
+    const pkv_status st = check_pool(pool);
+    return st != PKV_OK ? st : PKV_ERR_NULL;
+  }
+  return decode_call(pool, q, q_dtype, num_tables, q_len, num_q_heads, block_table, table_stride, kv_lens,
+                     max_kv_len, sm_scale, out, out_dtype, out_lse, workspace, workspace_bytes, 1, stream, false,
+                     new_k, new_v, new_tok_stride, new_head_stride);
 }
 // ---------------------------------------------------------------------------
 size_t pkv_attn_prefill_workspace_bytes(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads,

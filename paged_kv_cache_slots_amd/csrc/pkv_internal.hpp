@@ -38,8 +38,14 @@ struct ScatterParams {
   uint8_t* pool_k;
   uint8_t* pool_v;
   const int64_t* src_idx;   // nullable
-  const int64_t* slots;
+  const int64_t* slots;     // NULL in append mode
   const int64_t* slots2;    // nullable
+  // append mode (table != NULL): token x = t q_len + j goes to logical key
+  // lens[t] - q_len + j of table row t (skipped when that key is negative)
+  const int32_t* table;
+  const int32_t* lens;
+  int32_t table_stride;
+  int32_t q_len;
   int64_t n_tokens;
   int64_t src_tok_stride_b;   // bytes
   int64_t src_head_stride_b;  // bytes
@@ -64,6 +70,13 @@ struct DecodeParams {
   float* ws_o;                // [splits, T, n, Hq, D] when splits > 1
   float* ws_lse;              // [splits, T, n, Hq]
   int32_t* ws_cum;            // stream-K: [T + 1] prefix sums of tiles per table row
+  // nullable: the step's tokens [T * rows_per_table, Hkv, D] (pool element
+  // type, 16-byte aligned rows and strides), written by the head-parallel
+  // stream-K kernel into the row's last rows_per_table keys before it reads them
+  const uint8_t* new_k;
+  const uint8_t* new_v;
+  int64_t new_tok_stride_b;
+  int64_t new_head_stride_b;
   int64_t page_stride;        // elements
   int32_t page_shift;
   int32_t num_kv_heads;
@@ -203,6 +216,11 @@ namespace pkv {
 
 // Launchers: return hipGetLastError() of their launch.
 hipError_t launch_scatter(const ScatterParams& p, int vec_bytes, hipStream_t stream);
+// Whether the stream-K decode runs its head-parallel kernel (one 16-row
+// block per unit, kv heads in quads), the one that can write a step's tokens.
+inline bool sk_head_parallel(int waves_per_worker, int row_groups, int num_kv_heads) {
+  return waves_per_worker == 1 && row_groups == 1 && num_kv_heads % 4 == 0;
+}
 hipError_t launch_decode_mfma(const DecodeParams& p, ElemType kv, int head_dim, hipStream_t stream);
 int sk_waves_per_worker(int rows_per_unit);
 hipError_t launch_decode_sk(const DecodeParams& p, ElemType kv, int head_dim, int sm_count, hipStream_t stream);

@@ -27,7 +27,16 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
     const uint32_t rem = (uint32_t)(w - tok * per_tok);
     const uint32_t h = rem / (uint32_t)p.vecs_per_row;
     const uint32_t v = rem - h * (uint32_t)p.vecs_per_row;
-    const int64_t s1 = p.slots[tok];
+    int64_t s1;
+    if (p.table) {
+      const int64_t t = tok / p.q_len;
+      const int key = p.lens[t] - p.q_len + (int)(tok - t * p.q_len);
+      s1 = key < 0 ? -1
+                   : ((int64_t)p.table[t * p.table_stride + (key >> p.page_shift)] << p.page_shift) +
+                         (key & (int)mask);
+    } else {
+      s1 = p.slots[tok];
+    }
     const int64_t s2 = p.slots2 ? p.slots2[tok] : -1;
     if (s1 < 0 && s2 < 0) continue;
     const int64_t src_row = p.src_idx ? p.src_idx[tok] : tok;

@@ -322,6 +322,41 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
                                          hipStream_t stream);
 
 /*
+ * pkv_attn_decode_shared_prefix_append -- an n-sample step that writes its
+ * tokens' K/V into the tails and attends, in one call.
+ * [P5] commits on the n-sample path (the shared prefix read once per group,
+ * every sample's private tail) and the FA4 tail commit (the step's K/V goes
+ * into the row's pages first, then is attended causally).
+ *
+ * new_k, new_v: the step's tokens, element type of the pool, rows
+ * [groups * samples * q_len, num_kv_heads, head_dim] with token stride
+ * new_tok_stride and kv-head stride new_head_stride (elements; the head_dim
+ * elements of a row contiguous).  Token j of sample r (row r * q_len + j) is
+ * tail key tail_lens[r] - q_len + j: it is written, bytes untouched, into
+ * that key's slot (page tail_table[r][key / page_size], row key % page_size),
+ * and then every argument and result is that of
+ * pkv_attn_decode_shared_prefix over the updated pool.  Tokens whose key
+ * would be negative are not written.  The slots written must belong to the
+ * call alone: no prefix key and no other tail key maps to them.
+ * When a sample's rows fit 64 (q_len * num_q_heads / num_kv_heads <= 64) and
+ * new_k / new_v and their strides are 16-byte aligned, the tail workgroups
+ * write the tokens themselves (no separate launch); otherwise a scatter
+ * kernel runs first.  Either way the pool holds the tokens when the call's
+ * work on the stream is done.
+ * Errors: NULL new_k or new_v -> PKV_ERR_NULL; negative strides ->
+ * PKV_ERR_SHAPE; the rest as pkv_attn_decode_shared_prefix.
+ */
+pkv_status pkv_attn_decode_shared_prefix_append(const pkv_pool* pool, const void* new_k, const void* new_v,
+                                                int64_t new_tok_stride, int64_t new_head_stride, const void* q,
+                                                pkv_dtype q_dtype, int32_t groups, int32_t samples, int32_t q_len,
+                                                int32_t num_q_heads, const int32_t* prefix_table,
+                                                int32_t prefix_stride, const int32_t* prefix_lens,
+                                                int32_t max_prefix_len, const int32_t* tail_table,
+                                                int32_t tail_stride, const int32_t* tail_lens, int32_t max_tail_len,
+                                                float sm_scale, void* out, pkv_dtype out_dtype, float* out_lse,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pkv_attn_prefill_block_causal -- paged prefill with causal blocks.
  * [P1] Description / Cache (frame-causal attention needs no mask: the new
  * tokens are cut into causal blocks, each with its own key count, full

@@ -33,7 +33,8 @@ EXPORTED = ["pkv_status_string", "pkv_abi_version", "pkv_scatter_slots", "pkv_at
             "pkv_window_evicted_tokens", "pkv_causal_layout", "pkv_attn_decode_step",
             "pkv_attn_decode_shared_prefix_workspace_bytes", "pkv_attn_decode_shared_prefix", "pkv_check_slots",
             "pkv_check_tables", "pkv_attn_decode_noalloc", "pkv_attn_prefill_block_causal_ragged",
-            "pkv_set_timing_events", "pkv_xcd_ids", "pkv_attn_decode_append"]
+            "pkv_set_timing_events", "pkv_xcd_ids", "pkv_attn_decode_append",
+            "pkv_attn_decode_shared_prefix_append"]
 
 
 class PkvError(RuntimeError):
@@ -83,6 +84,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_attn_decode_shared_prefix_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "pkv_attn_decode_shared_prefix": (ctypes.c_int, [PP, P, ctypes.c_int, I32, I32, I32, I32, P, I32, P, I32, P,
                                                          I32, P, I32, F32, P, ctypes.c_int, P, P, SZ, P]),
+        "pkv_attn_decode_shared_prefix_append": (ctypes.c_int, [PP, P, P, I64, I64, P, ctypes.c_int, I32, I32, I32,
+                                                                I32, P, I32, P, I32, P, I32, P, I32, F32, P,
+                                                                ctypes.c_int, P, P, SZ, P]),
         "pkv_check_slots": (ctypes.c_int, [PP, P, I64, P, P]),
         "pkv_check_tables": (ctypes.c_int, [PP, P, I32, P, I32, P, P]),
         "pkv_attn_prefill_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
@@ -280,6 +284,41 @@ def pkv_attn_decode_shared_prefix(pool: Pool, q: torch.Tensor, samples: int, pre
         prefix_table.data_ptr(), prefix_table.stride(0), prefix_lens.data_ptr(), int(max_prefix_len),
         tail_table.data_ptr(), tail_table.stride(0), tail_lens.data_ptr(), int(max_tail_len), float(sm_scale),
         out.data_ptr(), _dtype_code(out.dtype), _ptr(out_lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
+
+
+def pkv_attn_decode_shared_prefix_append(pool: Pool, new_k: torch.Tensor, new_v: torch.Tensor, q: torch.Tensor,
+                                         samples: int, prefix_table: torch.Tensor, prefix_lens: torch.Tensor,
+                                         max_prefix_len: int, tail_table: torch.Tensor, tail_lens: torch.Tensor,
+                                         max_tail_len: int, sm_scale: float, out: torch.Tensor,
+                                         workspace: torch.Tensor, out_lse: Optional[torch.Tensor] = None,
+                                         stream=None) -> None:
+    """Write the step's K/V into the tails and run the n-sample step:
+    ``new_k`` / ``new_v`` [groups * samples * q_len, Hkv, D] (or
+    [groups * samples, q_len, Hkv, D]) in the pool's element type, rows of D
+    contiguous; token j of sample r becomes tail key tail_lens[r] - q_len + j,
+    then as ``pkv_attn_decode_shared_prefix``."""
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    if not prefix_table.is_contiguous() or not tail_table.is_contiguous():
+        raise ValueError("tables must be contiguous")
+    rows, q_len, hq, d = q.shape
+    if rows % samples:
+        raise ValueError("q rows must be groups * samples")
+    hkv = pool.k.shape[-2]
+    nk, nv = new_k.reshape(-1, hkv, d), new_v.reshape(-1, hkv, d)
+    if nk.shape[0] != rows * q_len or nv.shape != nk.shape or nk.stride() != nv.stride() or nk.stride(2) != 1:
+        raise ValueError("new_k / new_v must be [groups * samples * q_len, Hkv, D] with matching strides and "
+                         "contiguous rows")
+    if nk.element_size() != pool.k.element_size():
+        raise ValueError("new_k / new_v must have the pool's element type")
+    ps = pool.struct()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("pkv_attn_decode_shared_prefix_append", load_library().pkv_attn_decode_shared_prefix_append(
+        ctypes.byref(ps), nk.data_ptr(), nv.data_ptr(), nk.stride(0), nk.stride(1), q.data_ptr(),
+        _dtype_code(q.dtype), rows // samples, samples, q_len, hq, prefix_table.data_ptr(), prefix_table.stride(0),
+        prefix_lens.data_ptr(), int(max_prefix_len), tail_table.data_ptr(), tail_table.stride(0),
+        tail_lens.data_ptr(), int(max_tail_len), float(sm_scale), out.data_ptr(), _dtype_code(out.dtype),
+        _ptr(out_lse), workspace.data_ptr(), ws_bytes, _stream(stream)))
 
 
 def pkv_attn_prefill_workspace_bytes(batch: int, s_q: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

@@ -478,6 +478,68 @@ __device__ __forceinline__ int row_limit(const DecodeParams& p, int len, int qi)
 
 }  // namespace
 
+// Write the step's tokens at keys [kb, ke) of table row t (key x is step
+// token x - (len - n)) for kv head g into the pool: 16 bytes per thread and
+// instruction, threads i0, i0 + ni, ... of the caller's range; then wait
+// until this thread's stores have completed.
+template <int D, bool kFp8>
+__device__ __forceinline__ void append_rows(const DecodeParams& p, int t, int g, int len, int kb, int ke, int i0,
+                                            int ni) {
+  constexpr int esz = kFp8 ? 1 : 2;
+  constexpr int CPR = D * esz / 16;   // 16-byte chunks per row
+  const int n = p.rows_per_table;
+  const int row_b = p.num_kv_heads * D * esz;
+  const int64_t page_stride_b = p.page_stride * esz;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  uint8_t* kp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_pool));
+  uint8_t* vp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_pool));
+  for (int i = i0; i < (ke - kb) * CPR; i += ni) {
+    const int key = kb + i / CPR, c = i % CPR;
+    const int64_t src = (int64_t)(t * n + key - (len - n)) * p.new_tok_stride_b + (int64_t)g * p.new_head_stride_b + 16 * c;
+    const int64_t dst = (int64_t)trow[key >> p.page_shift] * page_stride_b + (int64_t)(key & pmask) * row_b +
+                        (int64_t)g * D * esz + 16 * c;
+    *reinterpret_cast<u32x4*>(kp + dst) = *reinterpret_cast<const u32x4*>(p.new_k + src);
+    *reinterpret_cast<u32x4*>(vp + dst) = *reinterpret_cast<const u32x4*>(p.new_v + src);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Up to 64 of the step's 16-byte chunks (keys [kb, ke) of table row t, kv
+// head g; one per lane) held in registers until the walk issues the loads of
+// the tile that holds them, and their pool offset (-1: none for this lane).
+struct StepTokens {
+  u32x4 k = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+  int64_t dst = -1;
+};
+
+template <int D, bool kFp8>
+__device__ __forceinline__ StepTokens load_step_tokens(const DecodeParams& p, int t, int g, int len, int kb, int ke) {
+  constexpr int esz = kFp8 ? 1 : 2;
+  constexpr int CPR = D * esz / 16;
+  const int lane = threadIdx.x & 63;
+  StepTokens tk;
+  if (lane < (ke - kb) * CPR) {
+    const int n = p.rows_per_table;
+    const int key = kb + lane / CPR, c = lane % CPR;
+    const int64_t src = (int64_t)(t * n + key - (len - n)) * p.new_tok_stride_b + (int64_t)g * p.new_head_stride_b + 16 * c;
+    tk.k = *reinterpret_cast<const u32x4*>(p.new_k + src);
+    tk.v = *reinterpret_cast<const u32x4*>(p.new_v + src);
+    const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+    tk.dst = (int64_t)trow[key >> p.page_shift] * p.page_stride * esz +
+             (int64_t)(key & ((1 << p.page_shift) - 1)) * p.num_kv_heads * D * esz + (int64_t)g * D * esz + 16 * c;
+  }
+  return tk;
+}
+
+__device__ __forceinline__ void store_step_tokens(const DecodeParams& p, const StepTokens& tk) {
+  if (tk.dst >= 0) {
+    *reinterpret_cast<u32x4*>(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_pool)) + tk.dst) = tk.k;
+    *reinterpret_cast<u32x4*>(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_pool)) + tk.dst) = tk.v;
+  }
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Split kernel: one workgroup per (key split, kv head, table row, row group).
 // Used without a stream-K workspace; with splits == 1 it needs no workspace.
@@ -513,6 +575,36 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   reset_state(st);
   const int first = tb + wp;
   const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
+  // The step's tokens, when the call writes them (keys len - n .. len - 1 of
+  // this split's keys; kv head g): the launch gives every (table row, kv
+  // head) one workgroup, so only this workgroup reads them.  With one row
+  // block (WP == 4) the wave that walks a token's tile is its only reader:
+  // it loads up to 64 16-byte chunks (4 tokens of 128 bf16 dims) now and
+  // stores them just before it issues that tile's loads, as the head-parallel
+  // stream-K kernel does.  With several row blocks every wave reads each tile,
+  // so the workgroup writes the tokens and meets at a barrier first.
+  int hook_tile = -1;
+  StepTokens tok;
+  if (p.new_k) {
+    constexpr int CPR = D * (kFp8 ? 1 : 2) / 16;   // 16-byte chunks per row
+    const int kb = max(max(len - p.rows_per_table, 0), tb * 32), ke = min(len, te * 32);
+    if constexpr (WP == 4) {
+      // the token tiles are at most 2 consecutive ones (n <= 16 rows): the
+      // one this wave walks, if any
+      const int t0 = kb >> 5;
+      const int kt = t0 + (((wp - (t0 - tb)) % WP) + WP) % WP;
+      const int wb = max(kb, kt * 32), we = min(ke, kt * 32 + 32);
+      if (wb < we && (we - wb) * CPR <= 64) {
+        tok = load_step_tokens<D, kFp8>(p, t, g, len, wb, we);
+        hook_tile = kt;
+      } else if (wb < we) {
+        append_rows<D, kFp8>(p, t, g, len, wb, we, lane, 64);
+      }
+    } else {
+      if (kb < ke) append_rows<D, kFp8>(p, t, g, len, kb, ke, threadIdx.x, blockDim.x);
+      __syncthreads();
+    }
+  }
   if constexpr (WP == 1 && D == 128 && !kFp8) {
     // four row blocks of one unit: every wave walks (the workgroup shares each tile through LDS)
     if (n_mine > 0)
@@ -521,7 +613,8 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   } else {
     if (rb * 16 < R && n_mine > 0)
       walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                          row_limit(p, len, 0), first, WP, n_mine);
+                          row_limit(p, len, 0), first, WP, n_mine, hook_tile,
+                          [&]() { store_step_tokens(p, tok); });
   }
 
   st.l += __shfl_xor(st.l, 16, 64);
@@ -617,32 +710,6 @@ __global__ __launch_bounds__(256, 2) void shared_prefix_kernel(DecodeParams pre,
   }
 }
 
-// Write the step's tokens at keys [kb, ke) of table row t (key x is step
-// token x - (len - n)) for kv head g into the pool: 16 bytes per lane and
-// instruction, then wait until the stores have completed.
-template <int D, bool kFp8>
-__device__ __forceinline__ void append_rows(const DecodeParams& p, int t, int g, int len, int kb, int ke) {
-  constexpr int esz = kFp8 ? 1 : 2;
-  constexpr int CPR = D * esz / 16;   // 16-byte chunks per row
-  const int lane = threadIdx.x & 63;
-  const int n = p.rows_per_table;
-  const int row_b = p.num_kv_heads * D * esz;
-  const int64_t page_stride_b = p.page_stride * esz;
-  const int pmask = (1 << p.page_shift) - 1;
-  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
-  uint8_t* kp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k_pool));
-  uint8_t* vp = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.v_pool));
-  for (int i = lane; i < (ke - kb) * CPR; i += 64) {
-    const int key = kb + i / CPR, c = i % CPR;
-    const int64_t src = (int64_t)(t * n + key - (len - n)) * p.new_tok_stride_b + (int64_t)g * p.new_head_stride_b + 16 * c;
-    const int64_t dst = (int64_t)trow[key >> p.page_shift] * page_stride_b + (int64_t)(key & pmask) * row_b +
-                        (int64_t)g * D * esz + 16 * c;
-    *reinterpret_cast<u32x4*>(kp + dst) = *reinterpret_cast<const u32x4*>(p.new_k + src);
-    *reinterpret_cast<u32x4*>(vp + dst) = *reinterpret_cast<const u32x4*>(p.new_v + src);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Head-parallel stream-K worker (units of one 16-row block; kv heads a
 // multiple of 4): a workgroup is one worker whose 4 waves take kv heads
 // 4 hg .. 4 hg + 3 of the same keys.  The flattened positions are (table row
@@ -720,7 +787,7 @@ __device__ __forceinline__ void decode_sk_heads(const DecodeParams& p, const int
         }
         hook_tile = kb / 32;
       } else if (kb < ke) {
-        append_rows<D, kFp8>(p, t, g, len, kb, ke);
+        append_rows<D, kFp8>(p, t, g, len, kb, ke, lane, 64);
       }
     }
     auto store_tokens = [&]() {

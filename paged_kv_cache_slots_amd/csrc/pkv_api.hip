@@ -403,16 +403,21 @@ size_t pkv_attn_decode_shared_prefix_workspace_bytes(int32_t groups, int32_t sam
   return (size_t)(states * rows * num_q_heads * (int64_t)(head_dim + 1) * (int64_t)sizeof(float));
 }
 
-pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t groups,
-                                         int32_t samples, int32_t q_len, int32_t num_q_heads,
-                                         const int32_t* prefix_table, int32_t prefix_stride,
-                                         const int32_t* prefix_lens, int32_t max_prefix_len,
-                                         const int32_t* tail_table, int32_t tail_stride, const int32_t* tail_lens,
-                                         int32_t max_tail_len, float sm_scale, void* out, pkv_dtype out_dtype,
-                                         float* out_lse, void* workspace, size_t workspace_bytes,
-                                         hipStream_t stream) {
+// One n-sample step; with new_k / new_v the step's tokens are written into
+// the tails' last q_len keys first (by the tail workgroups themselves when
+// one workgroup covers each (tail, kv head), else by an append-mode scatter).
+static pkv_status shared_call(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t groups,
+                              int32_t samples, int32_t q_len, int32_t num_q_heads, const int32_t* prefix_table,
+                              int32_t prefix_stride, const int32_t* prefix_lens, int32_t max_prefix_len,
+                              const int32_t* tail_table, int32_t tail_stride, const int32_t* tail_lens,
+                              int32_t max_tail_len, float sm_scale, void* out, pkv_dtype out_dtype, float* out_lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              const void* new_k = nullptr, const void* new_v = nullptr, int64_t new_tok_stride = 0,
+                              int64_t new_head_stride = 0) {
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
+  const bool append = new_k != nullptr || new_v != nullptr;
+  if (append && (new_tok_stride < 0 || new_head_stride < 0)) return PKV_ERR_SHAPE;
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype)) return PKV_ERR_DTYPE;
   if (groups < 0 || samples < 1 || q_len < 1 || num_q_heads < 1 || prefix_stride < 1 || tail_stride < 1 ||
       max_prefix_len < 0 || max_tail_len < 0 || !(sm_scale > 0.f) || sm_scale > 3.0e38f)
@@ -424,6 +429,7 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
   if ((int64_t)groups * samples * q_len > INT32_MAX / 2) return PKV_ERR_SHAPE;
   if (groups == 0) return PKV_OK;   // empty tensors may carry NULL pointers
   if (!q || !prefix_table || !prefix_lens || !tail_table || !tail_lens || !out || !workspace) return PKV_ERR_NULL;
+  if (append && (!new_k || !new_v)) return PKV_ERR_NULL;
   const int D = pool->head_dim;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (pool->page_size < 16) return PKV_ERR_UNSUPPORTED;
@@ -488,6 +494,22 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
   tail.splits = 1;
   tail.tiles_per_split = (int)std::max<int64_t>(1, ceil_div(max_tail_len, 32));
   tail.causal = 1;
+  if (append) {
+    // one tail workgroup per (sample, kv head) while its rows fit 64 (4 row
+    // blocks): it writes its own tokens; otherwise scatter them first
+    const bool fused = (int64_t)q_len * tail.group <= 64 && aligned(new_k, 16) && aligned(new_v, 16) &&
+                       (new_tok_stride * es) % 16 == 0 && (new_head_stride * es) % 16 == 0;
+    if (fused) {
+      tail.new_k = static_cast<const uint8_t*>(new_k);
+      tail.new_v = static_cast<const uint8_t*>(new_v);
+      tail.new_tok_stride_b = new_tok_stride * es;
+      tail.new_head_stride_b = new_head_stride * es;
+    } else if (launch_scatter_rows(pool, new_k, new_v, new_tok_stride, new_head_stride, nullptr, nullptr, nullptr,
+                                   (int64_t)groups * samples * q_len, tail_table, tail_lens, tail_stride, q_len,
+                                   stream) != hipSuccess) {
+      return PKV_ERR_HIP;
+    }
+  }
 
   if (launch_shared_prefix(pre, tail, elem_type(pool->dtype), D, stream) != hipSuccess) return PKV_ERR_HIP;
   MergeParams m;
@@ -504,6 +526,37 @@ pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pk
   m.keys_per_state = 1;
   m.out_bf16 = out_dtype == PKV_BF16;
   return launch_merge(m, stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_attn_decode_shared_prefix(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t groups,
+                                         int32_t samples, int32_t q_len, int32_t num_q_heads,
+                                         const int32_t* prefix_table, int32_t prefix_stride,
+                                         const int32_t* prefix_lens, int32_t max_prefix_len,
+                                         const int32_t* tail_table, int32_t tail_stride, const int32_t* tail_lens,
+                                         int32_t max_tail_len, float sm_scale, void* out, pkv_dtype out_dtype,
+                                         float* out_lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  return shared_call(pool, q, q_dtype, groups, samples, q_len, num_q_heads, prefix_table, prefix_stride, prefix_lens,
+                     max_prefix_len, tail_table, tail_stride, tail_lens, max_tail_len, sm_scale, out, out_dtype,
+                     out_lse, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_attn_decode_shared_prefix_append(const pkv_pool* pool, const void* new_k, const void* new_v,
+                                                int64_t new_tok_stride, int64_t new_head_stride, const void* q,
+                                                pkv_dtype q_dtype, int32_t groups, int32_t samples, int32_t q_len,
+                                                int32_t num_q_heads, const int32_t* prefix_table,
+                                                int32_t prefix_stride, const int32_t* prefix_lens,
+                                                int32_t max_prefix_len, const int32_t* tail_table,
+                                                int32_t tail_stride, const int32_t* tail_lens, int32_t max_tail_len,
+                                                float sm_scale, void* out, pkv_dtype out_dtype, float* out_lse,
+                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (groups > 0 && !new_k && !new_v) {   // (one of the two NULL is caught by shared_call)
+    const pkv_status st = check_pool(pool);
+    return st != PKV_OK ? st : PKV_ERR_NULL;
+  }
+  return shared_call(pool, q, q_dtype, groups, samples, q_len, num_q_heads, prefix_table, prefix_stride, prefix_lens,
+                     max_prefix_len, tail_table, tail_stride, tail_lens, max_tail_len, sm_scale, out, out_dtype,
+                     out_lse, workspace, workspace_bytes, stream, new_k, new_v, new_tok_stride, new_head_stride);
 }
 
 pkv_status pkv_attn_decode_step(const pkv_pool* pool, const void* q, pkv_dtype q_dtype, int32_t num_tables,

@@ -77,6 +77,35 @@ __device__ __forceinline__ PageWindow fetch_pages(const DecodeParams& p, const i
   return w;
 }
 
+// The same window read without the row's length, so that it can be loaded
+// together with it: entries for tiles below te, where te only bounds the
+// table row (tile te - 1 starts inside its table_stride pages), and a second
+// half's page outside the row is the first half's.  Entries past the row's
+// last key are padding; a page id outside the pool is clamped into it, so
+// that every id in the window names a real page (the tiles past the last key
+// are never walked; rows of a walked tile past it are masked).
+template <bool kFp8>
+__device__ __forceinline__ PageWindow fetch_pages_ahead(const DecodeParams& p, const int32_t* trow, int g, int first,
+                                                        int step, int te) {
+  const int lane = threadIdx.x & 63;
+  const int tile = first + lane * step;
+  PageWindow w{0, 0, 1.f, 1.f, 1.f, 1.f};
+  if (tile < te) {
+    const int key0 = tile * 32;
+    const uint32_t last = (uint32_t)(p.num_pages - 1);
+    w.e0 = (int)min((uint32_t)trow[key0 >> p.page_shift], last);
+    const int i1 = (key0 + 16) >> p.page_shift;
+    w.e1 = (p.page_shift >= 5 || i1 >= p.table_stride) ? w.e0 : (int)min((uint32_t)trow[i1], last);
+    if constexpr (kFp8) {
+      w.ks0 = p.k_scale[(int64_t)w.e0 * p.num_kv_heads + g];
+      w.vs0 = p.v_scale[(int64_t)w.e0 * p.num_kv_heads + g];
+      w.ks1 = p.k_scale[(int64_t)w.e1 * p.num_kv_heads + g];
+      w.vs1 = p.v_scale[(int64_t)w.e1 * p.num_kv_heads + g];
+    }
+  }
+  return w;
+}
+
 __device__ __forceinline__ int rl(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
 __device__ __forceinline__ float rlf(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
@@ -303,13 +332,15 @@ __device__ __forceinline__ void reset_state(RowState<D>& st) {
 // vector load; inside a window every tile is prefetched one step ahead with
 // unconditional loads (zero-range descriptor past the window's end).
 // hook() runs once, just before the loads of tile hook_tile are issued.
+// win0, when given, is the first window, already loaded.
 struct NoHook {
   __device__ void operator()() const {}
 };
 template <int D, bool kFp8, typename Hook = NoHook>
 __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
                                            const int32_t* trow, int g, int len, int lim, int lim_lo, int first,
-                                           int step, int n, int hook_tile = -1, Hook hook = Hook{}) {
+                                           int step, int n, int hook_tile = -1, Hook hook = Hook{},
+                                           const PageWindow* win0 = nullptr) {
   constexpr int esz = kFp8 ? 1 : 2;
   const int lane = threadIdx.x & 63;
   const int r_lane = lane & 15, j = lane >> 4;
@@ -324,7 +355,7 @@ __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D /
   const int te = first + (n - 1) * step + 1;   // one past the last tile walked
   TileRegs<D, kFp8> A, B;
   for (int w0 = 0; w0 < n; w0 += 64) {
-    const PageWindow win = fetch_pages<kFp8>(p, trow, g, first + w0 * step, step, te, len);
+    const PageWindow win = (win0 && w0 == 0) ? *win0 : fetch_pages<kFp8>(p, trow, g, first + w0 * step, step, te, len);
     const int n_win = n - w0 < 64 ? n - w0 : 64;
     auto issue = [&](TileRegs<D, kFp8>& X, int k) {
       const bool ok = k < n_win;
@@ -363,7 +394,7 @@ __device__ __forceinline__ void walk_tiles(RowState<D>& st, const u32x4 (&q)[D /
 template <int D>
 __device__ __forceinline__ void walk_tiles_shared(RowState<D>& st, const u32x4 (&q)[D / 32], const DecodeParams& p,
                                                   const int32_t* trow, int g, int len, int lim, int lim_lo,
-                                                  int first, int step, int n) {
+                                                  int first, int step, int n, const PageWindow* win0 = nullptr) {
   static_assert(D == 128, "the shared walk stages bf16 tiles of 128 dims");
   using T = TileRegs<D, false>;
   static_assert(T::KLD == 4 && T::VB == 16, "16 register slots of 16 bytes per lane");
@@ -413,7 +444,7 @@ __device__ __forceinline__ void walk_tiles_shared(RowState<D>& st, const u32x4 (
   };
   T r;
   for (int w0 = 0; w0 < n; w0 += 64) {
-    const PageWindow win = fetch_pages<false>(p, trow, g, first + w0 * step, step, te, len);
+    const PageWindow win = (win0 && w0 == 0) ? *win0 : fetch_pages<false>(p, trow, g, first + w0 * step, step, te, len);
     const int n_win = n - w0 < 64 ? n - w0 : 64;
     u32x4 xa[4], xb[4];
     issue(xa, win, w0, 0, n_win);
@@ -558,12 +589,13 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   const int rb = rg * WR + wr;
 
   const int len = p.kv_lens[t];
-  const int tiles = (len + 31) >> 5;
   const int tb = s * p.tiles_per_split;
-  int te = tb + p.tiles_per_split;
-  te = te < tiles ? te : tiles;
-  if (p.splits > 1 && tb >= te && !p.write_state) return;   // empty split: the merge never reads it
-
+  const int first = tb + wp;
+  const int32_t* trow = p.table + (int64_t)t * p.table_stride;
+  // Q and this wave's first window of page ids do not depend on the length:
+  // they are loaded together with it (the window bounded by the split and
+  // the table row instead), which takes one memory round trip off the
+  // workgroup's start.
   const int r = rb * 16 + r_lane;
   const bool row_ok = r < R;
   int qi;
@@ -571,9 +603,15 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   row_of(p, t, g, row_ok ? r : 0, qi, qrow);
   u32x4 q[D / 32];
   load_q<D, kFp8>(q, p, qrow, row_ok);
+  const int cap = (int)min((int64_t)tb + p.tiles_per_split, (((int64_t)p.table_stride << p.page_shift) + 31) >> 5);
+  const PageWindow win0 = fetch_pages_ahead<kFp8>(p, trow, g, first, WP, cap);
+  const int tiles = (len + 31) >> 5;
+  int te = tb + p.tiles_per_split;
+  te = te < tiles ? te : tiles;
+  if (p.splits > 1 && tb >= te && !p.write_state) return;   // empty split: the merge never reads it
+
   RowState<D> st;
   reset_state(st);
-  const int first = tb + wp;
   const int n_mine = first < te ? (te - first + WP - 1) / WP : 0;
   // The step's tokens, when the call writes them (keys len - n .. len - 1 of
   // this split's keys; kv head g): the launch gives every (table row, kv
@@ -608,13 +646,12 @@ __device__ __forceinline__ void decode_block(const DecodeParams& p, int s, int g
   if constexpr (WP == 1 && D == 128 && !kFp8) {
     // four row blocks of one unit: every wave walks (the workgroup shares each tile through LDS)
     if (n_mine > 0)
-      walk_tiles_shared<D>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                           row_limit(p, len, 0), first, 1, n_mine);
+      walk_tiles_shared<D>(st, q, p, trow, g, len, row_limit(p, len, qi), row_limit(p, len, 0), first, 1, n_mine,
+                           &win0);
   } else {
     if (rb * 16 < R && n_mine > 0)
-      walk_tiles<D, kFp8>(st, q, p, p.table + (int64_t)t * p.table_stride, g, len, row_limit(p, len, qi),
-                          row_limit(p, len, 0), first, WP, n_mine, hook_tile,
-                          [&]() { store_step_tokens(p, tok); });
+      walk_tiles<D, kFp8>(st, q, p, trow, g, len, row_limit(p, len, qi), row_limit(p, len, 0), first, WP, n_mine,
+                          hook_tile, [&]() { store_step_tokens(p, tok); }, &win0);
   }
 
   st.l += __shfl_xor(st.l, 16, 64);

@@ -337,6 +337,7 @@ static pkv_status decode_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
     p.ws_lse = p.ws_o + (int64_t)plan.splits * rows * num_q_heads * D;
   }
   p.page_stride = pool->page_stride;
+  p.num_pages = pool->num_pages;
   p.page_shift = log2i(pool->page_size);
   p.num_kv_heads = pool->num_kv_heads;
   p.num_tables = num_tables;
@@ -466,6 +467,7 @@ static pkv_status shared_call(const pkv_pool* pool, const void* q, pkv_dtype q_d
   pre.new_tok_stride_b = 0;
   pre.new_head_stride_b = 0;
   pre.page_stride = pool->page_stride;
+  pre.num_pages = pool->num_pages;
   pre.page_shift = log2i(pool->page_size);
   pre.num_kv_heads = pool->num_kv_heads;
   pre.num_tables = groups;

@@ -95,6 +95,7 @@ struct DecodeParams {
   int32_t causal;             // rows of a table row are a step's tokens: row i sees len - (n - 1 - i) keys
   int32_t write_state;        // always leave the normalised state of split s in ws_o / ws_lse (empty too)
   float scale_log2;           // sm_scale * log2(e)
+  int64_t num_pages;          // pages in the pool (page ids read ahead of the lengths are clamped below it)
 };
 
 struct MergeParams {

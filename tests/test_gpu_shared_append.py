@@ -6,7 +6,8 @@ oracle's n-sample step over that pool.  The cases cover tail workgroups of one
 row block (the wave that walks a token's tile writes it), of two and four row
 blocks (the workgroup writes, then meets at a barrier), samples whose rows
 need several tail workgroups (scatter first), tokens across a tile boundary,
-tails shorter than the step, and fp8 pools."""
+tails shorter than the step, 16-key pages (a tile's halves on two pages),
+tails longer than one 64-tile window of page ids, and fp8 pools."""
 
 import numpy as np
 import pytest
@@ -30,6 +31,8 @@ CASES = [
     ("tails_shorter_than_step", 1, 4, 5, [333], [1, 3, 5, 40], 8, 8, 128, 32, "bf16"),
     ("fp8_q4", 2, 4, 4, [1024, 100], (4, 260), 32, 8, 128, 32, "fp8"),
     ("fp8_q9_two_row_blocks", 1, 3, 9, [400], (9, 120), 8, 4, 128, 32, "fp8"),
+    ("q2_d64_ps16_half_tiles", 2, 3, 2, [300, 90], (2, 100), 8, 4, 64, 16, "bf16"),
+    ("tails_past_one_window", 1, 2, 1, [100], [9000, 8300], 32, 8, 128, 32, "bf16"),
 ]
 
 

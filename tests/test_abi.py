@@ -248,6 +248,51 @@ def test_decode_shared_prefix_argument_checks():
     assert call(p, G=0) == 0
 
 
+def test_decode_append_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+
+    def call(pool, **kw):
+        a = dict(nk=A, nv=A, ts=8 * 128, hs=128, q=A, qd=pkv.PKV_BF16, T=4, n=1, hq=32, table=A, tstride=128,
+                 lens=A, maxlen=4096, scale=0.1, out=A, od=pkv.PKV_BF16)
+        a.update(kw)
+        return lib.pkv_attn_decode_append(ctypes.byref(pool), a["nk"], a["nv"], a["ts"], a["hs"], a["q"], a["qd"],
+                                          a["T"], a["n"], a["hq"], a["table"], a["tstride"], a["lens"], a["maxlen"],
+                                          a["scale"], a["out"], a["od"], None, None, 0, None)
+    assert call(p, nk=None, nv=None) == 1
+    assert call(p, nk=None) == 1
+    assert call(p, nv=None) == 1
+    assert call(_pool(k=None), nk=None, nv=None) == 1    # the pool is checked first
+    assert call(p, ts=-1) == 2
+    assert call(p, hs=-1) == 2
+    assert call(p, hq=30) == 2
+    assert call(p, maxlen=128 * 32 + 1) == 2
+    assert call(p, qd=pkv.PKV_FP8_E4M3FN) == 4
+    assert call(p, T=0, nk=None, nv=None) == 0           # empty batch: OK, nothing launched
+
+
+def test_decode_shared_prefix_append_argument_checks():
+    lib = pkv.load_library()
+    p = _pool()
+
+    def call(pool, **kw):
+        a = dict(nk=A, nv=A, nts=8 * 128, nhs=128, q=A, qd=pkv.PKV_BF16, G=8, S=16, n=1, hq=32, pt=A, ps=64, pl=A,
+                 mp=2048, tt=A, ts=16, tl=A, mt=512, scale=0.1, out=A, od=pkv.PKV_BF16, ws=A, wsb=1 << 30)
+        a.update(kw)
+        return lib.pkv_attn_decode_shared_prefix_append(
+            ctypes.byref(pool), a["nk"], a["nv"], a["nts"], a["nhs"], a["q"], a["qd"], a["G"], a["S"], a["n"],
+            a["hq"], a["pt"], a["ps"], a["pl"], a["mp"], a["tt"], a["ts"], a["tl"], a["mt"], a["scale"], a["out"],
+            a["od"], None, a["ws"], a["wsb"], None)
+    assert call(p, nk=None, nv=None) == 1
+    assert call(p, nv=None) == 1
+    assert call(p, nts=-8) == 2
+    assert call(p, ws=None) == 1
+    assert call(p, mt=16 * 32 + 1) == 2
+    assert call(p, qd=pkv.PKV_F32) == 4
+    assert call(p, ws=A + 8) == 6
+    assert call(p, G=0, nk=None, nv=None) == 0
+
+
 def test_check_calls_argument_checks():
     lib = pkv.load_library()
     p = _pool()

@@ -136,3 +136,50 @@ def test_decode_append_equals_scatter_then_decode_bit_for_bit():
         results.append((from_dev(out), from_dev(lse), from_dev(pool.k), from_dev(pool.v)))
     for a, b in zip(*results):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("layout", ["packed_qkv_slice", "misaligned_by_one_element"])
+def test_decode_append_strided_token_rows(layout):
+    """The step's K/V as views: the K and V slices of a packed [T * q_len, Hq + 2 Hkv, D] projection (token
+    stride (Hq + 2 Hkv) D, 16-byte aligned: the kernel writes them itself), and rows that start one element
+    off a 16-byte boundary (the call scatters them first, 2 bytes at a time)."""
+    lens = [3, 31, 32, 33, 600, 1300]
+    hq, hkv, d, ps, n = 32, 8, 128, 32, 3
+    c = W.make_decode_case("strided_" + layout, 44, 1044, len(lens), hq, hkv, d, ps, lens, rows_per_table=n,
+                           new_per_seq=n, extra_table_cols=2,
+                           num_pool_pages=sum(math.ceil(L / ps) for L in lens) + 9)
+    note(f"decode append strided {layout} lens={lens} q_len={n}")
+    new_k, new_v, slots, k_start, v_start = step_tokens(c, n)
+    rows = new_k.shape[0]
+    if layout == "packed_qkv_slice":
+        packed = torch.zeros((rows, hq + 2 * hkv, d), dtype=torch.bfloat16, device=DEV)
+        packed[:, hq:hq + hkv] = to_dev(new_k)
+        packed[:, hq + hkv:] = to_dev(new_v)
+        dk, dv = packed[:, hq:hq + hkv], packed[:, hq + hkv:]
+        assert dk.stride() == ((hq + 2 * hkv) * d, d, 1)
+    else:
+        flat = torch.zeros(2 * rows * hkv * d + 2, dtype=torch.bfloat16, device=DEV)
+        dk = flat[1:1 + rows * hkv * d].view(rows, hkv, d)
+        dv = flat[1 + rows * hkv * d:1 + 2 * rows * hkv * d].view(rows, hkv, d)
+        dk.copy_(to_dev(new_k))
+        dv.copy_(to_dev(new_v))
+        assert dk.data_ptr() % 16 != 0
+    pool = pool_to_dev(c.pool)
+    q = to_dev(c.q)
+    t = q.shape[0]
+    out = torch.full((t, n, hq, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((t, n, hq), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(pkv.pkv_attn_decode_workspace_bytes(t, n, hq, hkv, d, c.max_kv_len), dtype=torch.uint8,
+                     device=DEV)
+    pkv.pkv_attn_decode_append(pool, dk, dv, q, to_dev(c.tables), to_dev(c.kv_lens), c.max_kv_len, c.sm_scale,
+                               out, lse, ws)
+    torch.cuda.synchronize()
+    live = slots >= 0
+    kp = orc.scatter_slots(k_start, new_k, slots[live], src_idx=np.nonzero(live)[0])
+    vp = orc.scatter_slots(v_start, new_v, slots[live], src_idx=np.nonzero(live)[0])
+    assert np.array_equal(from_dev(pool.k).view(np.uint8), kp.view(np.uint8)), "K pool differs from the scatter"
+    assert np.array_equal(from_dev(pool.v).view(np.uint8), vp.view(np.uint8)), "V pool differs from the scatter"
+    ref, ref_lse = orc.attn_decode_step(kp, vp, c.q, c.tables, c.kv_lens, c.sm_scale, kv_dtype="bf16",
+                                        q_dtype=c.q_dtype)
+    assert_close(as_f64(from_dev(out)), ref, "bf16", f"{layout} out")
+    assert_lse_close(from_dev(lse).astype(np.float64), ref_lse, "bf16", f"{layout} lse")

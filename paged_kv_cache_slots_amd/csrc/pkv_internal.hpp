@@ -1,5 +1,5 @@
 // Internal launch parameters and launchers of libpkv.  Host code validates the
-// public arguments (pkv_api.cpp) and then fills these plain structs, which the
+// public arguments (pkv_api.hip) and then fills these plain structs, which the
 // kernels take by value.
 #pragma once
 
@@ -232,6 +232,8 @@ hipError_t launch_shared_prefix(const DecodeParams& pre, const DecodeParams& tai
                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, int sm_count, hipStream_t stream);
+// The fp8 K/V prefill kernel alone on a grid of `grid` workgroups (prefill_fp8.hip).
+hipError_t launch_prefill_kernel_fp8(const PrefillParams& p, int grid, hipStream_t stream);
 int prefill_grid(int sm_count);
 int prefill_tail_units(int32_t batch, int32_t s_q, int32_t num_q_heads, int32_t num_kv_heads, int grid);
 hipError_t launch_rotate(const RotateParams& p, int elem_size, hipStream_t stream);

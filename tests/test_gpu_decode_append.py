@@ -183,3 +183,42 @@ def test_decode_append_strided_token_rows(layout):
                                         q_dtype=c.q_dtype)
     assert_close(as_f64(from_dev(out)), ref, "bf16", f"{layout} out")
     assert_lse_close(from_dev(lse).astype(np.float64), ref_lse, "bf16", f"{layout} lse")
+
+
+def test_decode_append_graph_replays():
+    """The call captured in a HIP graph (it allocates nothing and records no memset): every replay, with eager
+    work and synchronisations between them, gives the eager call's output bits and pool bytes."""
+    lens = [5, 40, 600, 1300]
+    hq, hkv, d, ps, n = 32, 8, 128, 32, 1
+    c = W.make_decode_case("graph", 45, 1045, len(lens), hq, hkv, d, ps, lens, rows_per_table=n, new_per_seq=n,
+                           extra_table_cols=2, num_pool_pages=sum(math.ceil(L / ps) for L in lens) + 9)
+    note(f"decode append graph replays lens={lens}")
+    new_k, new_v, _, _, _ = step_tokens(c, n)
+    pool = pool_to_dev(c.pool)
+    q, tables, kv_lens, nk, nv = to_dev(c.q), to_dev(c.tables), to_dev(c.kv_lens), to_dev(new_k), to_dev(new_v)
+    t = q.shape[0]
+    out = torch.zeros((t, n, hq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros((t, n, hq), dtype=torch.float32, device=DEV)
+    ws = torch.empty(pkv.pkv_attn_decode_workspace_bytes(t, n, hq, hkv, d, c.max_kv_len), dtype=torch.uint8,
+                     device=DEV)
+
+    def call(stream=None):
+        pkv.pkv_attn_decode_append(pool, nk, nv, q, tables, kv_lens, c.max_kv_len, c.sm_scale, out, lse, ws,
+                                   stream=stream)
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    ref_k, ref_v = pool.k.clone(), pool.v.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream())
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+        assert torch.equal(pool.k.view(torch.uint8), ref_k.view(torch.uint8))
+        assert torch.equal(pool.v.view(torch.uint8), ref_v.view(torch.uint8))

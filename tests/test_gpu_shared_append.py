@@ -144,3 +144,10 @@ def test_shared_append_equals_scatter_then_step_bit_for_bit():
         results.append((from_dev(out), from_dev(lse), from_dev(pool.k), from_dev(pool.v)))
     for a, b in zip(*results):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_shared_append_fp32_output_and_single_sample_groups():
+    """fp32 outputs, groups of one sample each (every tail its own group), and an empty prefix."""
+    tl = [7, 33, 64, 100, 1]
+    c = W.make_shared_step_case("fp32_out_single", 62, 1062, 5, 1, 1, [0, 40, 300, 64, 1000], tl, 16, 4, 128, 32)
+    check_append(c, out_dtype=torch.float32)

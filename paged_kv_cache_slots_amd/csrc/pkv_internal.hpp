@@ -71,8 +71,9 @@ struct DecodeParams {
   float* ws_lse;              // [splits, T, n, Hq]
   int32_t* ws_cum;            // stream-K: [T + 1] prefix sums of tiles per table row
   // nullable: the step's tokens [T * rows_per_table, Hkv, D] (pool element
-  // type, 16-byte aligned rows and strides), written by the head-parallel
-  // stream-K kernel into the row's last rows_per_table keys before it reads them
+  // type, 16-byte aligned rows and strides), written into the row's last
+  // rows_per_table keys, before they are read, by the workgroup that alone
+  // reads them (head-parallel stream-K decode; n-sample tails)
   const uint8_t* new_k;
   const uint8_t* new_v;
   int64_t new_tok_stride_b;
